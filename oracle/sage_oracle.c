@@ -1,0 +1,380 @@
+/*
+ * sage_oracle.c -- CPU oracle for the SageAttention2-style quantized attention
+ * forward ("sage2" in the pages' benchmark artefacts).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's cpu_baseline leg
+ * do.  It shares no code, header, table or constant with the HIP library: every
+ * block size, scale constant and layout arrives as a function argument.
+ *
+ * Plain, slow, obviously correct.  Floating point is fp64 except where the method
+ * itself fixes an fp32 decision (quantisation), where the same fp32 operation is
+ * written out.  Build with gcc -O2 -ffp-contract=off -fopenmp (no fast-math): the
+ * fp32 divisions, subtractions and nearbyintf calls below must be IEEE-exact.
+ *
+ * Sources.  The pages are three JSON benchmark artefacts of one repository:
+ *   [latency]  "gb10-sage2-p0-interleave-softmax-latency.json"
+ *   [profile]  "gb10-sampling-component-profile-1344x768-124f-seed440420.json"
+ *   [strided]  "gb10-sage-strided-nhd-summary-1344x768-124f-seed440420.json"
+ * They name the stages (profile, attention_internal_p50_milliseconds.sage2:
+ * qk_quantize, v_quantize, attention_forward, framework_and_k_smoothing_estimate),
+ * the shapes (latency, q_shape = [1, 37810, 56, 128]; h_msa_shape = [37810, 5376])
+ * and the strided NHD input / token-major output dataflow (strided, dataflow).
+ * They print no arithmetic.  The recipe written out here is SageAttention2's:
+ * INT8 Q/K with per-tile fp32 scales amax/127 and round-to-nearest-even, K
+ * smoothed by its per-head token mean, FP8 (OCP E4M3FN) V with per-channel
+ * scales amax/448, an online softmax over 64-key tiles and FP8 P.  Each reading
+ * taken where the method leaves a choice open is stated at the function.
+ *
+ * Parity of every function here is pinned by the CPU tests (library routines,
+ * closed forms, invariants, brute force); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef long long i64;
+
+/* ---------------------------------------------------------------- bf16 ---- */
+/* bfloat16 is the upper half of an IEEE binary32; widening is exact. */
+static float bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Element (b, n, h, d) of a [B, N, H, D] view with d-stride 1 and the other
+ * strides in elements (strided NHD views of the packed QKV buffer, or HND). */
+static float load_bf16(const uint16_t *base, i64 sb, i64 sn, i64 sh, int b, int n, int h, int d)
+{
+    return bf16_to_f32(base[(i64)b * sb + (i64)n * sn + (i64)h * sh + d]);
+}
+
+/* ---------------------------------------------------------- OCP E4M3FN ---- */
+/* OCP 8-bit floating point, E4M3 "FN" flavour: sign, 4 exponent bits (bias 7),
+ * 3 mantissa bits.  e = 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there
+ * is no infinity; the largest finite magnitude is S.1111.110 = 448. */
+double sage_oracle_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 0xF, m = c & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* Round the fp32 value x to E4M3FN: nearest, ties to even, magnitudes beyond
+ * 448 saturate to 448, the sign of zero is kept.  (Reading: the method's FP8 is
+ * the OCP E4M3FN encoding with saturating round-to-nearest-even.) */
+uint8_t sage_oracle_e4m3_encode(float x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    double a = fabs((double)x);
+    if (isnan(x))
+        return sign | 0x7F;
+    if (a >= 448.0)
+        return sign | 0x7E;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal grid: multiples of 2^-9; a*512 is exact in fp64 */
+        double q = nearbyint(a * 512.0); /* 0..8; 8 is the code of 2^-6 */
+        return sign | (uint8_t)q;
+    }
+    int e2;
+    frexp(a, &e2);        /* a = f * 2^e2, f in [0.5, 1) */
+    int E = e2 - 1;       /* a = (1 + mant) * 2^E, E in -6..8 */
+    double mant = a / ldexp(1.0, E) - 1.0;  /* exact */
+    double q = nearbyint(mant * 8.0);        /* ties to even; 0..8 */
+    if (q == 8.0) {
+        q = 0.0;
+        E += 1;
+    }
+    int code = ((E + 7) << 3) | (int)q;
+    if (code > 0x7E)
+        code = 0x7E;
+    return sign | (uint8_t)code;
+}
+
+void sage_oracle_e4m3_encode_array(const float *x, i64 n, uint8_t *out)
+{
+    for (i64 i = 0; i < n; i++)
+        out[i] = sage_oracle_e4m3_encode(x[i]);
+}
+
+void sage_oracle_e4m3_decode_array(const uint8_t *c, i64 n, double *out)
+{
+    for (i64 i = 0; i < n; i++)
+        out[i] = sage_oracle_e4m3_decode(c[i]);
+}
+
+/* ------------------------------------------------------------- K mean ---- */
+/* K smoothing statistic: the token mean of K per (batch, head, channel).
+ * Reading: summed in fp64, first over `chunk` consecutive tokens in ascending
+ * order, then the chunk partials in ascending order, then one division by N in
+ * fp64 and one rounding to fp32.  km has layout [B, H, D]. */
+void sage_oracle_kmean(const uint16_t *k, i64 sb, i64 sn, i64 sh,
+                       int B, int N, int H, int D, int chunk, float *km)
+{
+    int nchunks = (N + chunk - 1) / chunk;
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++)
+            for (int d = 0; d < D; d++) {
+                double total = 0.0;
+                for (int c = 0; c < nchunks; c++) {
+                    double part = 0.0;
+                    int n1 = (c + 1) * chunk < N ? (c + 1) * chunk : N;
+                    for (int n = c * chunk; n < n1; n++)
+                        part += (double)load_bf16(k, sb, sn, sh, b, n, h, d);
+                    total += part;
+                }
+                km[((i64)b * H + h) * D + d] = (float)(total / (double)N);
+            }
+}
+
+/* ------------------------------------------------------ INT8 blocks ---- */
+/* One quantisation block of `rows` tokens x D channels, values already fp32.
+ * scale = amax / 127 (one IEEE fp32 division); code = clamp(rne(x / scale),
+ * -127, 127) with x / scale one IEEE fp32 division and ties to even.  A block
+ * whose amax is 0 gets scale 0 and all-zero codes. */
+static void quant_block_int8(const float *x, int rows, int D, int8_t *codes, i64 code_row_stride,
+                             float *scale)
+{
+    float amax = 0.0f;
+    for (int r = 0; r < rows; r++)
+        for (int d = 0; d < D; d++)
+            amax = fmaxf(amax, fabsf(x[(i64)r * D + d]));
+    if (amax == 0.0f) {
+        *scale = 0.0f;
+        for (int r = 0; r < rows; r++)
+            for (int d = 0; d < D; d++)
+                codes[(i64)r * code_row_stride + d] = 0;
+        return;
+    }
+    float s = amax / 127.0f;
+    *scale = s;
+    for (int r = 0; r < rows; r++)
+        for (int d = 0; d < D; d++) {
+            float t = nearbyintf(x[(i64)r * D + d] / s);
+            if (t > 127.0f)
+                t = 127.0f;
+            if (t < -127.0f)
+                t = -127.0f;
+            codes[(i64)r * code_row_stride + d] = (int8_t)t;
+        }
+}
+
+/* Q quantisation: one scale per (batch, head, `blk` consecutive tokens); the
+ * last block of a head holds the N % blk remaining tokens.  codes [B, H, N, D]
+ * (logical, unpadded), scales [B, H, ceil(N / blk)]. */
+void sage_oracle_quant_q(const uint16_t *q, i64 sb, i64 sn, i64 sh,
+                         int B, int N, int H, int D, int blk, int8_t *codes, float *scales)
+{
+    int nblk = (N + blk - 1) / blk;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++)
+            for (int t = 0; t < nblk; t++) {
+                int n0 = t * blk, rows = (N - n0) < blk ? (N - n0) : blk;
+                float *x = (float *)malloc(sizeof(float) * (size_t)rows * D);
+                for (int r = 0; r < rows; r++)
+                    for (int d = 0; d < D; d++)
+                        x[(i64)r * D + d] = load_bf16(q, sb, sn, sh, b, n0 + r, h, d);
+                quant_block_int8(x, rows, D, codes + (((i64)b * H + h) * N + n0) * D, D,
+                                 scales + ((i64)b * H + h) * nblk + t);
+                free(x);
+            }
+}
+
+/* K quantisation after smoothing: x = (fp32) k - km[b, h, d] (one fp32
+ * subtraction, not re-rounded to bf16), then blocks of `blk` tokens exactly as
+ * for Q.  codes [B, H, N, D], scales [B, H, ceil(N / blk)]. */
+void sage_oracle_quant_k(const uint16_t *k, i64 sb, i64 sn, i64 sh,
+                         int B, int N, int H, int D, const float *km, int blk,
+                         int8_t *codes, float *scales)
+{
+    int nblk = (N + blk - 1) / blk;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++)
+            for (int t = 0; t < nblk; t++) {
+                int n0 = t * blk, rows = (N - n0) < blk ? (N - n0) : blk;
+                const float *m = km + ((i64)b * H + h) * D;
+                float *x = (float *)malloc(sizeof(float) * (size_t)rows * D);
+                for (int r = 0; r < rows; r++)
+                    for (int d = 0; d < D; d++)
+                        x[(i64)r * D + d] = load_bf16(k, sb, sn, sh, b, n0 + r, h, d) - m[d];
+                quant_block_int8(x, rows, D, codes + (((i64)b * H + h) * N + n0) * D, D,
+                                 scales + ((i64)b * H + h) * nblk + t);
+                free(x);
+            }
+}
+
+/* ------------------------------------------------------- V to E4M3 ---- */
+/* V quantisation: one scale per (batch, head, channel) over all N tokens,
+ * sv = amax / 448 (one IEEE fp32 division), code = E4M3FN(v / sv) with v / sv
+ * one IEEE fp32 division.  amax 0 gives sv 0 and codes 0x00.
+ * codes [B, H, N, D] (logical), scales [B, H, D]. */
+void sage_oracle_quant_v(const uint16_t *v, i64 sb, i64 sn, i64 sh,
+                         int B, int N, int H, int D, uint8_t *codes, float *scales)
+{
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < H; h++)
+            for (int d = 0; d < D; d++) {
+                float amax = 0.0f;
+                for (int n = 0; n < N; n++)
+                    amax = fmaxf(amax, fabsf(load_bf16(v, sb, sn, sh, b, n, h, d)));
+                float sv = amax / 448.0f;
+                uint8_t *c = codes + ((i64)b * H + h) * (i64)N * D + d;
+                scales[((i64)b * H + h) * D + d] = amax == 0.0f ? 0.0f : sv;
+                for (int n = 0; n < N; n++) {
+                    if (amax == 0.0f)
+                        c[(i64)n * D] = 0x00;
+                    else
+                        c[(i64)n * D] = sage_oracle_e4m3_encode(load_bf16(v, sb, sn, sh, b, n, h, d) / sv);
+                }
+            }
+}
+
+/* ------------------------------------------------ exact attention ---- */
+/* The plain definition: row i of softmax(Q K^T * sm_scale), computed in fp64
+ * from the bf16 inputs.  p receives the N normalised probabilities. */
+void sage_oracle_softmax_row(const uint16_t *q, i64 qsb, i64 qsn, i64 qsh,
+                             const uint16_t *k, i64 ksb, i64 ksn, i64 ksh,
+                             int N, int D, int b, int h, int i, double sm_scale, double *p)
+{
+    double m = -INFINITY, l = 0.0;
+    for (int j = 0; j < N; j++) {
+        double s = 0.0;
+        for (int d = 0; d < D; d++)
+            s += (double)load_bf16(q, qsb, qsn, qsh, b, i, h, d) *
+                 (double)load_bf16(k, ksb, ksn, ksh, b, j, h, d);
+        p[j] = s * sm_scale;
+        if (p[j] > m)
+            m = p[j];
+    }
+    for (int j = 0; j < N; j++) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+    }
+    for (int j = 0; j < N; j++)
+        p[j] /= l;
+}
+
+/* O = softmax(Q K^T * sm_scale) V for selected query rows; non-causal, no mask,
+ * all N keys.  rows[(b*H + h)*nrows + r] names the query row of output row r;
+ * out has layout [B, H, nrows, D]. */
+void sage_oracle_attn_exact(const uint16_t *q, i64 qsb, i64 qsn, i64 qsh,
+                            const uint16_t *k, i64 ksb, i64 ksn, i64 ksh,
+                            const uint16_t *v, i64 vsb, i64 vsn, i64 vsh,
+                            int B, int N, int H, int D, double sm_scale,
+                            const int *rows, int nrows, double *out)
+{
+#pragma omp parallel
+    {
+        double *p = (double *)malloc(sizeof(double) * (size_t)N);
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int b = 0; b < B; b++)
+            for (int h = 0; h < H; h++)
+                for (int r = 0; r < nrows; r++) {
+                    int i = rows[((i64)b * H + h) * nrows + r];
+                    double *o = out + (((i64)b * H + h) * nrows + r) * D;
+                    sage_oracle_softmax_row(q, qsb, qsn, qsh, k, ksb, ksn, ksh, N, D, b, h, i, sm_scale, p);
+                    for (int d = 0; d < D; d++) {
+                        double acc = 0.0;
+                        for (int j = 0; j < N; j++)
+                            acc += p[j] * (double)load_bf16(v, vsb, vsn, vsh, b, j, h, d);
+                        o[d] = acc;
+                    }
+                }
+        free(p);
+    }
+}
+
+/* ------------------------------------- quantised method, step by step ---- */
+/* The quantised forward as the method computes it, from the codes and scales
+ * (logical layouts as produced above: codes [B, H, N, D], Q/K scales
+ * [B, H, ceil(N / qblk or kblk)], V scales [B, H, D]):
+ *   a_ij = sum_d qc_id * kc_jd                      exact integer
+ *   s_ij = a_ij * sq[i / qblk] * sk[j / kblk] * sm_scale
+ *   for key tiles of `ptile` keys in ascending order (the last one partial):
+ *     m_t   = max(m_{t-1}, max_j s_ij)              m_{-1} = -inf
+ *     alpha = exp(m_{t-1} - m_t)
+ *     p_ij  = exp(s_ij - m_t)
+ *     l     = alpha * l + sum_j p_ij                unrounded p
+ *     pq_ij = E4M3FN(fp32(pscale * p_ij))           (if round_p; else pscale * p)
+ *     acc_d = alpha * acc_d + sum_j pq_ij * E4M3FN^-1(vc_jd)
+ *   o_id = acc_d * sv_d / (pscale * l)
+ * Readings: P is rounded relative to the running maximum after each tile (no
+ * thresholded rescaling, no split over keys); the normaliser sums P before it
+ * is rounded; pscale (448) maps p in (0, 1] onto the E4M3 range and is divided
+ * out at the end.  round_p = 0 keeps P unrounded; the pins use it to check the
+ * tile walk on inputs that quantise exactly. */
+void sage_oracle_attn_method(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
+                             const uint8_t *vc, const float *vs,
+                             int B, int N, int H, int D, int qblk, int kblk, int ptile,
+                             double sm_scale, double pscale, int round_p,
+                             const int *rows, int nrows, double *out)
+{
+    int nqb = (N + qblk - 1) / qblk, nkb = (N + kblk - 1) / kblk;
+    double vdec[256];
+    for (int c = 0; c < 256; c++)
+        vdec[c] = sage_oracle_e4m3_decode((uint8_t)c);
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)ptile);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int b = 0; b < B; b++)
+            for (int h = 0; h < H; h++)
+                for (int r = 0; r < nrows; r++) {
+                    i64 bh = (i64)b * H + h;
+                    int i = rows[bh * nrows + r];
+                    const int8_t *qi = qc + (bh * N + i) * D;
+                    double sq = qs[bh * nqb + i / qblk];
+                    double m = -INFINITY, l = 0.0;
+                    for (int d = 0; d < D; d++)
+                        acc[d] = 0.0;
+                    for (int j0 = 0; j0 < N; j0 += ptile) {
+                        int j1 = j0 + ptile < N ? j0 + ptile : N;
+                        double mt = m;
+                        for (int j = j0; j < j1; j++) {
+                            const int8_t *kj = kc + (bh * N + j) * D;
+                            i64 a = 0;
+                            for (int d = 0; d < D; d++)
+                                a += (i64)qi[d] * (i64)kj[d];
+                            s[j - j0] = (double)a * sq * (double)ks[bh * nkb + j / kblk] * sm_scale;
+                            if (s[j - j0] > mt)
+                                mt = s[j - j0];
+                        }
+                        double alpha = exp(m - mt); /* m = -inf on the first tile: 0 */
+                        l *= alpha;
+                        for (int d = 0; d < D; d++)
+                            acc[d] *= alpha;
+                        for (int j = j0; j < j1; j++) {
+                            double p = exp(s[j - j0] - mt);
+                            double pq = round_p ? sage_oracle_e4m3_decode(
+                                                      sage_oracle_e4m3_encode((float)(pscale * p)))
+                                                : pscale * p;
+                            const uint8_t *vj = vc + (bh * N + j) * D;
+                            l += p;
+                            for (int d = 0; d < D; d++)
+                                acc[d] += pq * vdec[vj[d]];
+                        }
+                        m = mt;
+                    }
+                    double *o = out + (bh * nrows + r) * D;
+                    for (int d = 0; d < D; d++)
+                        o[d] = acc[d] * (double)vs[bh * D + d] / (pscale * l);
+                }
+        free(s);
+        free(acc);
+    }
+}

@@ -1,0 +1,232 @@
+"""Pins of the oracle's attention: the exact fp64 softmax attention against
+torch's scaled_dot_product_attention (fp64, CPU) and against invariants and
+closed forms; the step-by-step quantised method against the exact result on
+inputs that quantise exactly, and against hand-computed single- and two-tile
+cases that fix where P is rounded."""
+import math
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from quantized_softmax_attention_amd import inputs
+from tests.helpers import bnhd, oracle_view
+
+SM = 1.0 / math.sqrt(128.0)
+
+
+def _sdpa64(q, k, v, scale):
+    """Library reference: torch SDPA in fp64 on the CPU.  Inputs [B, N, H, D]."""
+    t = lambda x: x.double().permute(0, 2, 1, 3).contiguous()
+    return F.scaled_dot_product_attention(t(q), t(k), t(v), scale=scale).numpy()   # [B, H, N, D]
+
+
+def _exact(q, k, v, scale=SM, rows=None):
+    return oracle.attn_exact(oracle_view(q), oracle_view(k), oracle_view(v), scale, rows)
+
+
+# --------------------------------------------------------------- exact
+@pytest.mark.parametrize("B,N,H,D", [(1, 1, 1, 4), (1, 5, 2, 4), (2, 37, 3, 16), (1, 130, 2, 128)])
+def test_exact_matches_library_sdpa(B, N, H, D):
+    c = inputs.hnd_case(B, N, H, D=D, seed=N)
+    sc = 1.0 / math.sqrt(D)
+    got = _exact(c.q, c.k, c.v, sc)
+    ref = _sdpa64(c.q, c.k, c.v, sc)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_exact_on_packed_strided_views_equals_hnd():
+    c = inputs.packed_case(1, 70, 3, D=128, seed=1)
+    hnd = [t.transpose(1, 2).contiguous().transpose(1, 2) for t in (c.q, c.k, c.v)]
+    assert np.array_equal(_exact(c.q, c.k, c.v), _exact(*hnd))
+    ref = _sdpa64(c.q, c.k, c.v, SM)
+    assert np.max(np.abs(_exact(c.q, c.k, c.v) - ref)) < 1e-12
+
+
+def test_softmax_rows_sum_to_one_and_match_library():
+    c = inputs.hnd_case(1, 300, 2, D=128, seed=11)
+    for (h, i) in [(0, 0), (1, 17), (1, 299)]:
+        p = oracle.softmax_row(oracle_view(c.q), oracle_view(c.k), 0, h, i, SM)
+        assert abs(p.sum() - 1.0) <= 1e-14
+        s = (c.q[0, i, h].double() @ c.k[0, :, h].double().T) * SM
+        assert np.max(np.abs(p - torch.softmax(s, 0).numpy())) <= 1e-15
+
+
+def test_exact_uniform_v_gives_that_v():
+    c = inputs.hnd_case(1, 200, 2, D=8, seed=2)
+    u = np.array([0.5, -1.25, 3.0, 0.0, -0.0078125, 7.5, 1.0, -2.0], np.float32)
+    v = bnhd(np.broadcast_to(u, (1, 200, 2, 8)))
+    o = _exact(c.q, c.k, v)
+    assert np.max(np.abs(o - u)) <= 1e-13
+
+
+def test_exact_invariant_to_constant_added_to_k():
+    rng = np.random.default_rng(3)
+    q = rng.integers(-3, 4, (1, 50, 2, 8)).astype(np.float32) / 2
+    k = rng.integers(-3, 4, (1, 50, 2, 8)).astype(np.float32) / 2
+    v = rng.normal(size=(1, 50, 2, 8)).astype(np.float32)
+    shift = rng.integers(-20, 21, (1, 1, 2, 8)).astype(np.float32)
+    v = torch.from_numpy(v).to(torch.bfloat16)
+    a = _exact(bnhd(q), bnhd(k), v, 0.5)
+    b = _exact(bnhd(q), bnhd(k + shift), v, 0.5)
+    assert np.max(np.abs(a - b)) <= 1e-12
+
+
+def test_exact_closed_forms():
+    c = inputs.hnd_case(1, 64, 1, D=16, seed=4)
+    # N = 1: the output is v_0
+    o1 = _exact(c.q[:, :1], c.k[:, :1], c.v[:, :1], 0.25)
+    assert np.array_equal(o1[0, 0, 0], c.v[0, 0, 0].double().numpy())
+    # Q = 0: the output is the column mean of V
+    z = torch.zeros_like(c.q)
+    o = _exact(z, c.k, c.v, 0.25)
+    mean = c.v[0, :, 0].double().mean(0).numpy()
+    assert np.max(np.abs(o[0, 0] - mean)) <= 1e-14
+    # two keys with logit gap 2 * 0.5: o = (v0 + e v1) / (1 + e)
+    q = np.zeros((1, 2, 1, 4), np.float32); q[..., 0] = 1
+    k = np.zeros((1, 2, 1, 4), np.float32); k[0, 1, 0, 0] = 2
+    v = np.zeros((1, 2, 1, 4), np.float32); v[0, 0, 0] = [1, 0, 2, -1]; v[0, 1, 0] = [0, 1, -4, 3]
+    o = _exact(bnhd(q), bnhd(k), bnhd(v), 0.5)[0, 0, 0]
+    v64 = v.astype(np.float64)
+    want = (v64[0, 0, 0] + math.e * v64[0, 1, 0]) / (1 + math.e)
+    assert np.max(np.abs(o - want)) <= 1e-15
+
+
+def test_exact_permutation_equivariance_and_dominant_key():
+    c = inputs.hnd_case(1, 96, 2, D=32, seed=6)
+    perm = torch.randperm(96, generator=torch.Generator().manual_seed(0))
+    base = _exact(c.q, c.k, c.v, 0.2)
+    kp = c.k[:, perm].contiguous(); vp = c.v[:, perm].contiguous()
+    assert np.max(np.abs(_exact(c.q, kp, vp, 0.2) - base)) <= 1e-13
+    qp = c.q[:, perm].contiguous()
+    assert np.max(np.abs(_exact(qp, c.k, c.v, 0.2) - base[:, :, perm.numpy()])) <= 1e-13
+    # a key aligned with the query and 40 logits above the rest selects its value row
+    q = np.zeros((1, 9, 1, 4), np.float32); q[0, :, 0, 0] = 1
+    k = np.zeros((1, 9, 1, 4), np.float32); k[0, 6, 0, 0] = 40
+    v = np.arange(36, dtype=np.float32).reshape(1, 9, 1, 4)
+    o = _exact(bnhd(q), bnhd(k), bnhd(v), 1.0)
+    assert np.max(np.abs(o[0, 0] - v[0, 6, 0])) <= 1e-12
+
+
+def test_exact_row_selection():
+    c = inputs.hnd_case(2, 40, 2, D=16, seed=8)
+    full = _exact(c.q, c.k, c.v, 0.25)
+    rows = np.array([[[39, 0, 7], [5, 5, 38]], [[1, 2, 3], [39, 38, 37]]], np.int32)
+    part = _exact(c.q, c.k, c.v, 0.25, rows)
+    for b in range(2):
+        for h in range(2):
+            assert np.array_equal(part[b, h], full[b, h, rows[b, h]])
+
+
+# -------------------------------------------------------------- method
+def _exactly_quantisable(N, H, D, seed):
+    """Q, K, V whose quantisation is lossless: integer Q/K codes with a +-127 in
+    every block (power-of-two scales), K with zero token mean, V of E4M3 values
+    with a +-448 * 2^e in every channel."""
+    rng = np.random.default_rng(seed)
+    q = rng.integers(-127, 128, (1, N, H, D)).astype(np.float32)
+    for t in range(0, N, 32):
+        q[0, t, :, 0] = 127
+    q *= 2.0 ** -7
+    half = rng.integers(-127, 128, (1, N // 2, H, D)).astype(np.float32)
+    half[0, 0, :, 1] = -127
+    k = np.concatenate([half, -half], axis=1)               # zero mean per channel
+    for t in range(0, N, 64):                                # +-127 in every 64-block
+        k[0, t, :, 2] = 127 if t < N // 2 else -127
+        src = t - N // 2 if t >= N // 2 else t + N // 2
+        k[0, src, :, 2] = -k[0, t, :, 2]
+    k *= 2.0 ** -5
+    assert np.all(k.sum(axis=1) == 0)
+    table = oracle.e4m3_decode(np.arange(0x7F))
+    v = rng.choice(np.concatenate([table, -table]), (1, N, H, D)).astype(np.float32)
+    v[0, 0, :, :] = 448.0
+    v *= 2.0 ** -6
+    return bnhd(q), bnhd(k), bnhd(v)
+
+
+def _quantise(q, k, v):
+    km = oracle.kmean(oracle_view(k))
+    qc, qs = oracle.quant_q(oracle_view(q), 32)
+    kc, ks = oracle.quant_k(oracle_view(k), km, 64)
+    vc, vs = oracle.quant_v(oracle_view(v))
+    return qc, qs, kc, ks, vc, vs
+
+
+@pytest.mark.parametrize("N", [64, 150, 256])
+def test_method_without_p_rounding_equals_exact_on_lossless_inputs(N):
+    q, k, v = _exactly_quantisable(N, 2, 16, seed=N)
+    qc, qs, kc, ks, vc, vs = _quantise(q, k, v)
+    assert np.all(qs == 2.0 ** -7) and np.all(ks == 2.0 ** -5) and np.all(vs == 2.0 ** -6)
+    got = oracle.attn_method(qc, qs, kc, ks, vc, vs, 0.25, round_p=False)
+    ref = _exact(q, k, v, 0.25)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_method_single_tile_hand_computed():
+    # one query, two keys, D = 1, sm_scale 1: s = [0, ks1] with ks1 = fp32(ln 0.3)
+    ks1 = np.float32(math.log(0.3))
+    qc = np.ones((1, 1, 2, 1), np.int8); qs = np.ones((1, 1, 1), np.float32)
+    kc = np.array([0, 1], np.int8).reshape(1, 1, 2, 1); ks = np.array([[[ks1]]], np.float32)
+    vc = np.array([0x38, 0xB4], np.uint8).reshape(1, 1, 2, 1)     # 1.0 and -0.75 in E4M3
+    vs = np.array([[[0.5]]], np.float32)
+    o = oracle.attn_method(qc, qs, kc, ks, vc, vs, 1.0, rows=np.zeros((1, 1, 1), np.int32))
+    p1 = math.exp(float(ks1))                                  # ~0.3; 448 * p1 ~ 134.4 -> 128
+    want = (448 * 1.0 + 128 * -0.75) * 0.5 / (448 * (1 + p1))
+    assert abs(o[0, 0, 0, 0] - want) <= 1e-15
+
+
+def test_method_p_rounded_against_running_max_per_tile():
+    # 70 keys, D = 1: tile 0 (keys 0..63) all s = 0; tile 1 holds key 64 with s = 3
+    # and keys 65..69 with s = 0.  Tile 0's P is rounded against max 0 (448 each),
+    # then rescaled by e^-3; tile 1 rounds 448 e^-3 = 22.30 -> 22.
+    N = 70
+    qc = np.ones((1, 1, N, 1), np.int8); qs = np.ones((1, 1, 3), np.float32)
+    kc = np.zeros((1, 1, N, 1), np.int8); kc[0, 0, 64, 0] = 1
+    ks = np.array([[[1.0, 3.0]]], np.float32)
+    vals = np.array([0x30, 0x38, 0x40, 0xB8], np.uint8)     # 0.5, 1, 2, -1
+    vc = vals[np.arange(N) % 4].reshape(1, 1, N, 1)
+    vd = np.array([0.5, 1.0, 2.0, -1.0])[np.arange(N) % 4]
+    vs = np.array([[[1.0]]], np.float32)
+    o = oracle.attn_method(qc, qs, kc, ks, vc, vs, 1.0, rows=np.zeros((1, 1, 1), np.int32))[0, 0, 0, 0]
+    a = math.exp(-3.0)
+    acc = a * 448 * vd[:64].sum() + 448 * vd[64] + 22 * vd[65:].sum()
+    l = a * 64 + 1 + 5 * a
+    assert abs(o - acc / (448 * l)) <= 1e-14
+    # rounding at the final maximum instead would give a different value
+    alt = (22 * vd[:64].sum() + 448 * vd[64] + 22 * vd[65:].sum()) / (448 * l)
+    assert abs(o - alt) > 1e-3
+
+
+def test_method_closed_forms_n1_q0_uniform_v():
+    c = inputs.hnd_case(1, 100, 2, D=128, seed=12)
+    qc, qs, kc, ks, vc, vs = _quantise(c.q, c.k, c.v)
+    vdq = oracle.e4m3_decode(vc).reshape(vc.shape) * vs[:, :, None, :]
+    # N = 1: the dequantised v_0
+    o1 = oracle.attn_method(qc[:, :, :1], qs[:, :, :1], kc[:, :, :1], ks[:, :, :1], vc[:, :, :1], vs, SM)
+    assert np.max(np.abs(o1[:, :, 0] - vdq[:, :, 0])) <= 1e-15 * np.max(np.abs(vdq))
+    # Q = 0: every p is 1 exactly, so the output is the mean of the dequantised V
+    o0 = oracle.attn_method(np.zeros_like(qc), qs, kc, ks, vc, vs, SM)
+    assert np.max(np.abs(o0 - vdq.mean(axis=2, keepdims=True))) <= 1e-14
+    # uniform V: every channel is +-448 * sv, the output is that times one common factor
+    u = ((np.arange(128) - 63.5) / 8).astype(np.float32)
+    vu = bnhd(np.broadcast_to(u, (1, 100, 2, 128)).copy())
+    vcu, vsu = oracle.quant_v(oracle_view(vu))
+    assert np.all((vcu & 0x7F) == 0x7E)
+    ou = oracle.attn_method(qc, qs, kc, ks, vcu, vsu, SM)
+    vdq_u = oracle.e4m3_decode(vcu).reshape(vcu.shape) * vsu[:, :, None, :]
+    ratio = ou / vdq_u
+    assert np.max(np.abs(ratio - ratio[..., :1])) <= 1e-13
+    assert np.all(np.abs(ratio - 1) <= 1.0 / 16)
+
+
+def test_method_error_floor_on_gaussian_inputs():
+    # the quantised method is an approximation: on N(0,1) inputs its distance to
+    # the exact result sits in a narrow band set by 3-bit E4M3 mantissas
+    c = inputs.config("tiny")
+    qc, qs, kc, ks, vc, vs = _quantise(c.q, c.k, c.v)
+    got = oracle.attn_method(qc, qs, kc, ks, vc, vs, SM)
+    ref = _exact(c.q, c.k, c.v)
+    err = oracle.rel_l2(got, ref)
+    assert 0.02 < err < 0.06, err
