@@ -1,0 +1,261 @@
+"""Benchmark of the quantised attention forward on one MI355X.
+
+One step = the whole quantised path over one resident batch: qk_quantize (with
+K smoothing), v_quantize, and the fused INT8-QK / FP8-PV attention, on the
+block-24 workload B=1, N=37810, H=56, D=128 (Q/K/V strided views of a packed
+bf16 [N, 3*56*128] projection buffer, token-major [N, 7168] bf16 output).
+Inputs are seeded synthetic stand-ins (N(0,1); K with a per-channel N(0,2)
+offset) for the real activations the benchmark artefacts measured.
+
+Prints ONE JSON line.  Besides the contract keys it carries:
+  roofline      -- the attention kernel (dominant) against the INT8/FP8 MFMA peak;
+                   its duration is measured with HIP events on its own stream.
+  stages        -- per-stage ms and the quantisers' achieved HBM bandwidth.
+  bf16_path     -- the unquantised BF16-MFMA path on the same inputs.
+  cpu_baseline  -- the CPU oracle (quantisers in full + step-by-step quantised
+                   attention on sampled rows, extrapolated), on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOPS (4·N²·d·H/t) + ms/call at N=37810,H=56,d=128; % MFMA peak"
+PEAK_I8F8_TFLOPS = 5000.0      # MI355X dense INT8 (POP/s) and FP8 (FLOP/s)
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+B, N, H, D = 1, 37810, 56, 128
+
+
+def attn_flops(b=B, n=N, h=H, d=D) -> float:
+    return 4.0 * b * n * n * d * h
+
+
+def quant_bytes(b=B, n=N, h=H, d=D) -> dict:
+    """Algorithmic HBM bytes of the quantisers (each input read as the kernels
+    must, each output written once)."""
+    e = b * n * h * d
+    npad = (n + 255) // 256 * 256
+    codes = b * h * npad * d
+    return {
+        # K read for the mean, Q and K read for the codes, int8 codes written
+        "qk_quantize": 2 * e + 2 * 2 * e + 2 * codes,
+        # V read for the channel maxima, V read again for the codes, fp8 codes written
+        "v_quantize": 2 * e + 2 * e + codes,
+    }
+
+
+def attn_bytes(b=B, n=N, h=H, d=D) -> int:
+    """Algorithmic HBM bytes of one attention launch: Q, K, V codes read once,
+    the bf16 output written once (scales are negligible)."""
+    npad = (n + 255) // 256 * 256
+    return 3 * b * h * npad * d + 2 * b * n * h * d
+
+
+def source_hash(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_src: str):
+    """Measured HBM traffic of the attention kernel from committed counter runs,
+    only if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "attn_i8f8_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(case, rows_per_head=256, heads=4):
+    """Time the oracle: quantisers at full size, then the step-by-step
+    quantised attention on `rows_per_head` sampled rows of `heads` heads,
+    extrapolated to the whole call."""
+    import numpy as np
+
+    import oracle
+    from quantized_softmax_attention_amd import inputs
+    from tests.helpers import oracle_view
+
+    q, k, v = (oracle_view(t) for t in (case.q, case.k, case.v))
+    t0 = time.perf_counter()
+    km = oracle.kmean(k)
+    qc, qs = oracle.quant_q(q, 32)
+    kc, ks = oracle.quant_k(k, km, 64)
+    vc, vs = oracle.quant_v(v)
+    t_quant = time.perf_counter() - t0
+    rows = inputs.sample_rows(case.B, case.H, case.N, count=rows_per_head, tail=64)[:, :heads]
+    sub = lambda a: np.ascontiguousarray(a[:, :heads])
+    t0 = time.perf_counter()
+    oracle.attn_method(sub(qc), sub(qs), sub(kc), sub(ks), sub(vc), sub(vs), 1.0 / math.sqrt(D), rows)
+    t_attn = time.perf_counter() - t0
+    scale = (case.N * case.H) / (rows_per_head * heads)
+    t_call = t_quant + t_attn * scale
+    return {
+        "value": attn_flops(case.B, case.N, case.H, case.D) / t_call / 1e12,
+        "unit": "TFLOP/s",
+        "ms_per_call_extrapolated": t_call * 1e3,
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": ("quantisers at full size (%.2f s measured) + step-by-step quantised attention on %d sampled "
+                   "rows x %d heads against all %d keys (%.2f s measured), attention time extrapolated x%.1f "
+                   "to %d rows x %d heads" % (t_quant, rows_per_head, heads, case.N, t_attn, scale, case.N,
+                                              case.H)),
+    }
+
+
+def stats_ms(xs):
+    xs = sorted(xs)
+    pick = lambda p: xs[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]
+    return {"mean": statistics.fmean(xs), "p50": pick(0.5), "p90": pick(0.9), "min": xs[0], "max": xs[-1],
+            "count": len(xs)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--bf16-calls", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also launch one plain 1 GiB device copy (for HBM counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (heads would shard with no "
+              "exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_softmax_attention_amd import inputs, sage
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sage.lib()                       # fail loudly if the HIP library is missing
+
+    t0 = time.perf_counter()
+    case = inputs.config("block24")
+    gen_s = time.perf_counter() - t0
+    g = case.to(dev)
+    buf = sage.Buffers(B, N, H, device=dev)
+    out = sage.token_major_out(B, N, H, device=dev)
+    sm = 1.0 / math.sqrt(D)
+    stream = torch.cuda.Stream(device=dev)    # default priority
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        bcopy = torch.empty_like(a)
+        with torch.cuda.stream(stream):
+            bcopy.copy_(a)
+        stream.synchronize()
+        del a, bcopy
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        sage.sage_quantize_qk(g.q, g.k, buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.k_mean,
+                              buf.ws_qk, stream)
+        if evs is not None:
+            evs[1].record(stream)
+        sage.sage_quantize_v(g.v, buf.v_codes, buf.v_scale, buf.ws_v, stream)
+        if evs is not None:
+            evs[2].record(stream)
+        sage.sage_attn_fwd(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, out, sm,
+                           stream)
+        if evs is not None:
+            evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    stream.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    stream.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+
+    qk_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    v_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    at_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    ms_per_step = wall * 1e3 / args.steps
+    flops = attn_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    attn_mean = statistics.fmean(at_ms)
+    achieved = flops / (attn_mean * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "quantized_softmax_attention_amd", "csrc", "sage_attn.hip")
+    qb = quant_bytes()
+
+    # the bf16 comparison path on the same resident inputs
+    out16 = sage.token_major_out(B, N, H, device=dev)
+    e16 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.bf16_calls)]
+    sage.sage_attn_fwd_bf16(g.q, g.k, g.v, out16, sm, stream)
+    for e in e16:
+        e[0].record(stream)
+        sage.sage_attn_fwd_bf16(g.q, g.k, g.v, out16, sm, stream)
+        e[1].record(stream)
+    stream.synchronize()
+    bf16_ms = [e[0].elapsed_time(e[1]) for e in e16]
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8+fp8e4m3 (fp32 softmax/accumulate)",
+        "data": "synthetic (seeded N(0,1) Q/K/V, K + per-channel N(0,2) offset; stand-in for block-24 activations)",
+        "config": {"workload": "block24 quantised forward: B=1, N=37810, H=56, D=128, Q/K/V strided NHD views of "
+                               "a packed bf16 [37810, 21504] QKV buffer, token-major bf16 [37810, 7168] output",
+                   "B": B, "N": N, "H": H, "D": D, "layout": "strided_nhd", "non_causal": True},
+        "roofline": {"bound": "mfma", "kernel": "attn_i8f8_kernel", "achieved": achieved,
+                     "peak": PEAK_I8F8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_I8F8_TFLOPS,
+                     "traffic": load_traffic(kernel_src), "algorithmic_bytes": attn_bytes(),
+                     "flops_per_launch": flops, "ms_per_launch": attn_mean},
+        "stages": {
+            "qk_quantize_ms": stats_ms(qk_ms), "v_quantize_ms": stats_ms(v_ms), "attn_fwd_ms": stats_ms(at_ms),
+            "step_ms_events": stats_ms(step_ms),
+            "qk_quantize_GBps": qb["qk_quantize"] / (statistics.fmean(qk_ms) * 1e-3) / 1e9,
+            "v_quantize_GBps": qb["v_quantize"] / (statistics.fmean(v_ms) * 1e-3) / 1e9,
+            "hbm_peak_GBps": PEAK_HBM_GBS,
+            "attn_pct_of_i8f8_peak": 100.0 * achieved / PEAK_I8F8_TFLOPS,
+            "step_pct_of_i8f8_peak": 100.0 * value / PEAK_I8F8_TFLOPS,
+        },
+        "bf16_path": {"ms_per_call": stats_ms(bf16_ms),
+                      "tflops": flops / (statistics.fmean(bf16_ms) * 1e-3) / 1e12,
+                      "frac_of_bf16_peak": flops / (statistics.fmean(bf16_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "pages_context": {"gb10_attention_forward_p50_ms": 238.995, "gb10_total_excluding_layout_ms": 258.613,
+                          "note": "NVIDIA GB10 on real activations; context only"},
+        "input_generation_s": gen_s,
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * sage_mi355x.h -- C ABI of libsage_mi355x.so: the SageAttention2-style quantised
+ * softmax attention forward ("sage2") for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the dense, non-causal attention O = softmax(Q K^T * sm_scale) V
+ * of a video diffusion transformer block, B sequences of N packed tokens, H heads
+ * of D = 128 channels.  The pages this follows are benchmark artefacts that name
+ * its stages and shapes but print no arithmetic:
+ *   - "gb10-sampling-component-profile-1344x768-124f-seed440420.json",
+ *     attention_internal_p50_milliseconds.sage2: qk_quantize, v_quantize,
+ *     attention_forward, framework_and_k_smoothing_estimate (the four calls below
+ *     are those stages; the K smoothing statistic is computed inside
+ *     sage_quantize_qk);
+ *   - "gb10-sage2-p0-interleave-softmax-latency.json", q_shape [1, 37810, 56, 128]
+ *     and scheduler (64-key tiles, cta_k = 64; 32-query warps, warp_q = 32);
+ *   - "gb10-sage-strided-nhd-summary-1344x768-124f-seed440420.json", dataflow:
+ *     Q/K/V are read as strided views of the QKV projection output with no
+ *     materialising copy, and the output is written token-major for out_proj;
+ *     next_targets on the profile page asks for exactly such a dense kernel.
+ * The arithmetic is SageAttention2's: INT8 Q and K with per-block fp32 scales
+ * amax / 127 and round-to-nearest-even, K smoothed by its per-head token mean,
+ * OCP FP8 E4M3 V with per-channel scales amax / 448, an fp32 online softmax over
+ * 64-key tiles, and P rounded to E4M3 (as 448 * p) for the FP8 P.V product.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers; `stream` is a hipStream_t passed as
+ *     void* (NULL = the default stream).  Every call only enqueues work on
+ *     `stream`: the library never synchronises, allocates, frees or caches
+ *     device memory, holds no mutable global state and is re-entrant.  The
+ *     caller owns every buffer and keeps it alive until the work completes.
+ *   - bf16 inputs are [B, N, H, D] views with unit d-stride and element strides
+ *     (stride_b, stride_n, stride_h).  Contiguous HND, contiguous NHD and the
+ *     strided views of a packed [B, N, 3*H*D] projection buffer are all such views.
+ *   - Only D == SAGE_HEAD_DIM is supported.
+ *   - Code and scale buffers use Npad = sage_npad(N) = round_up(N, SAGE_N_ALIGN)
+ *     tokens; entries for tokens N..Npad-1 are written as zero.
+ *   - Errors: arguments are validated on the host before anything is enqueued
+ *     and a non-zero sage_status is returned (nothing is launched).  A failed
+ *     launch returns SAGE_ERR_HIP.  There is no fallback path.  NaN or infinite
+ *     inputs are outside the contract and are not checked.
+ */
+#ifndef SAGE_MI355X_H
+#define SAGE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_HEAD_DIM 128 /* channels per head */
+#define SAGE_Q_BLOCK 32   /* tokens per Q scale */
+#define SAGE_K_BLOCK 64   /* tokens per K scale (= keys per softmax tile) */
+#define SAGE_P_TILE 64    /* keys per online-softmax step; P is rounded per tile */
+#define SAGE_N_ALIGN 256  /* code buffers hold round_up(N, 256) tokens */
+
+typedef enum {
+    SAGE_OK = 0,
+    SAGE_ERR_NULL = 1,      /* a required pointer is NULL */
+    SAGE_ERR_SHAPE = 2,     /* B, N, H < 1, D != 128, or sizes overflow */
+    SAGE_ERR_STRIDE = 3,    /* strides let tokens or heads overlap */
+    SAGE_ERR_ALIGN = 4,     /* a pointer or stride breaks 16-byte alignment */
+    SAGE_ERR_WORKSPACE = 5, /* workspace too small */
+    SAGE_ERR_HIP = 6,       /* the HIP runtime reported an error */
+    SAGE_ERR_VALUE = 7      /* sm_scale is not finite and positive */
+} sage_status;
+
+/* A [B, N, H, D] bf16 view: element (b, n, h, d) is at
+ * data + b*stride_b + n*stride_n + h*stride_h + d (strides in elements).
+ * data must be 16-byte aligned and stride_n, stride_h multiples of 8 (so every
+ * 128-channel head row is 16-byte aligned); |stride_h| >= D and the views must
+ * not alias across (n, h).  Strides may not be negative. */
+typedef struct {
+    const void *data;
+    int64_t stride_b, stride_n, stride_h;
+} sage_bf16_in;
+
+typedef struct {
+    void *data;
+    int64_t stride_b, stride_n, stride_h;
+} sage_bf16_out;
+
+/* round_up(N, SAGE_N_ALIGN); 0 for N < 1. */
+int64_t sage_npad(int N);
+
+/* Bytes of device workspace sage_quantize_qk needs: ceil(N/64)*B*H*D doubles
+ * (per-64-token fp64 partial sums of K). */
+size_t sage_qk_workspace_bytes(int B, int N, int H, int D);
+
+/* Bytes of device workspace sage_quantize_v needs: ceil(N/256)*B*H*D floats
+ * (per-256-token partial channel maxima of |V|) plus B*H*D floats. */
+size_t sage_v_workspace_bytes(int B, int N, int H, int D);
+
+/* qk_quantize with K smoothing (profile page, attention_internal_p50_milliseconds
+ * .sage2: qk_quantize and framework_and_k_smoothing_estimate).
+ *   k_mean [B, H, D] fp32: the token mean of K per (b, h, d), summed in fp64 over
+ *     64-token chunks in ascending token order, the chunk sums in ascending
+ *     order, divided by N in fp64, rounded once to fp32.
+ *   q_codes [B, H, Npad, D] int8, q_scale [B, H, Npad/32] fp32: per (b, h, block
+ *     of 32 tokens) scale = amax/127 (IEEE fp32 division) and code =
+ *     clamp(rne(x / scale), -127, 127) with x / scale an IEEE fp32 division;
+ *     a block whose amax is 0 has scale 0 and zero codes.
+ *   k_codes [B, H, Npad, D] int8, k_scale [B, H, Npad/64] fp32: the same on
+ *     x = fp32(k) - k_mean[b, h, d] (one fp32 subtraction) with 64-token blocks.
+ *   workspace: >= sage_qk_workspace_bytes(B, N, H, D) bytes, 8-byte aligned;
+ *     contents on entry are ignored.
+ * Codes, scales and k_mean are bit-exactly defined by the above (no tolerance).
+ * q_codes/k_codes 16-byte aligned; scales and k_mean 4-byte aligned. */
+int sage_quantize_qk(const sage_bf16_in *q, const sage_bf16_in *k, int B, int N, int H, int D,
+                     int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale,
+                     float *k_mean, void *workspace, size_t workspace_bytes, void *stream);
+
+/* v_quantize (profile page, attention_internal_p50_milliseconds.sage2.v_quantize).
+ *   v_scale [B, H, D] fp32: sv = amax / 448 over all N tokens of the channel
+ *     (IEEE fp32 division; 0 when amax is 0).
+ *   v_codes: OCP E4M3FN codes of v / sv (IEEE fp32 division; round to nearest
+ *     even, saturating at +-448, sign of zero kept; 0x00 where sv is 0), stored
+ *     tile-major as the FP8 P.V operand: byte
+ *         (((b*H + h)*(Npad/64) + t)*128 + d)*64 + p
+ *     holds the code of token 64*t + kappa(p), channel d, where for p = 32*u + j
+ *     (u in {0, 1}, j in 0..31)
+ *         kappa(p) = 32*(j/16) + 8*((j%16)/4) + 4*u + (j%4).
+ *     Tokens N..Npad-1 hold 0x00.  v_codes 16-byte aligned.
+ *   workspace: >= sage_v_workspace_bytes(B, N, H, D) bytes, 4-byte aligned. */
+int sage_quantize_v(const sage_bf16_in *v, int B, int N, int H, int D,
+                    uint8_t *v_codes, float *v_scale, void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/* attention_forward (profile page, attention_internal_p50_milliseconds.sage2
+ * .attention_forward; latency page, the whole artefact): from the buffers the two
+ * calls above wrote, for every query i < N of every (b, h):
+ *   a_ij = sum_d qc_id * kc_jd (exact int32)
+ *   s_ij = a_ij * q_scale[i/32] * k_scale[j/64] * sm_scale (fp32)
+ *   for 64-key tiles in ascending order (the last one partial, keys >= N absent):
+ *     m  <- max(m, max_j s_ij);  rescale l and acc by exp(m_old - m)
+ *     p_ij = exp(s_ij - m);  l += p_ij (fp32, before rounding)
+ *     acc_d += E4M3(448 * p_ij) * E4M3^-1(vc_jd)   (FP8 MFMA, fp32 accumulate)
+ *   out[b, i, h, d] = bf16_rne(acc_d * v_scale[d] / (448 * l)).
+ * Results match that definition within floating-point tolerance (fp32 exp and
+ * accumulation order).  Rows >= N are not written.  out must be 8-byte aligned
+ * with stride_n, stride_h multiples of 4 (token-major [B, N, H*D] is the
+ * intended layout: stride_b = N*H*D, stride_n = H*D, stride_h = D).
+ * sm_scale must be finite and > 0 (1/sqrt(128) for the softmax). */
+int sage_attn_fwd(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes,
+                  const float *k_scale, const uint8_t *v_codes, const float *v_scale,
+                  int B, int N, int H, int D, float sm_scale, const sage_bf16_out *out,
+                  void *stream);
+
+/* The unquantised comparison path: the same softmax(Q K^T * sm_scale) V straight
+ * from the strided bf16 views, BF16 MFMA for Q K^T and P.V (P rounded to bf16),
+ * fp32 online softmax over 64-key tiles.  Output as sage_attn_fwd. */
+int sage_attn_fwd_bf16(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v,
+                       int B, int N, int H, int D, float sm_scale, const sage_bf16_out *out,
+                       void *stream);
+
+/* A static, human-readable name for a sage_status value. */
+const char *sage_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_MI355X_H */

@@ -50,6 +50,8 @@ def _load():
         if not os.path.exists(_LIB):
             build(force=False)
         lib = ctypes.CDLL(_LIB)
+        lib.sage_oracle_num_threads.restype = _int
+        lib.sage_oracle_num_threads.argtypes = []
         lib.sage_oracle_e4m3_decode.restype = _dbl
         lib.sage_oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.sage_oracle_e4m3_encode.restype = ctypes.c_uint8
@@ -110,6 +112,11 @@ class View:
 def _c(a, dtype):
     a = np.ascontiguousarray(a, dtype=dtype)
     return a, a.ctypes.data
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().sage_oracle_num_threads())
 
 
 # ------------------------------------------------------------------ codec

@@ -251,11 +251,12 @@ void sage_oracle_softmax_row(const uint16_t *q, i64 qsb, i64 qsn, i64 qsh,
                              int N, int D, int b, int h, int i, double sm_scale, double *p)
 {
     double m = -INFINITY, l = 0.0;
+    const uint16_t *qi = q + (i64)b * qsb + (i64)i * qsn + (i64)h * qsh;
     for (int j = 0; j < N; j++) {
+        const uint16_t *kj = k + (i64)b * ksb + (i64)j * ksn + (i64)h * ksh;
         double s = 0.0;
         for (int d = 0; d < D; d++)
-            s += (double)load_bf16(q, qsb, qsn, qsh, b, i, h, d) *
-                 (double)load_bf16(k, ksb, ksn, ksh, b, j, h, d);
+            s += (double)bf16_to_f32(qi[d]) * (double)bf16_to_f32(kj[d]);
         p[j] = s * sm_scale;
         if (p[j] > m)
             m = p[j];
@@ -287,12 +288,12 @@ void sage_oracle_attn_exact(const uint16_t *q, i64 qsb, i64 qsn, i64 qsh,
                     int i = rows[((i64)b * H + h) * nrows + r];
                     double *o = out + (((i64)b * H + h) * nrows + r) * D;
                     sage_oracle_softmax_row(q, qsb, qsn, qsh, k, ksb, ksn, ksh, N, D, b, h, i, sm_scale, p);
-                    for (int d = 0; d < D; d++) {
-                        double acc = 0.0;
-                        for (int j = 0; j < N; j++)
-                            acc += p[j] * (double)load_bf16(v, vsb, vsn, vsh, b, j, h, d);
-                        o[d] = acc;
-                    }
+                    /* o_d = sum_j p_j v_jd, each channel summed in ascending j */
+                    for (int d = 0; d < D; d++)
+                        o[d] = 0.0;
+                    for (int j = 0; j < N; j++)
+                        for (int d = 0; d < D; d++)
+                            o[d] += p[j] * (double)load_bf16(v, vsb, vsn, vsh, b, j, h, d);
                 }
         free(p);
     }
@@ -377,4 +378,17 @@ void sage_oracle_attn_method(const int8_t *qc, const float *qs, const int8_t *kc
         free(s);
         free(acc);
     }
+}
+
+/* Threads the OpenMP loops above use (reported beside oracle timings). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int sage_oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -1,0 +1,203 @@
+"""Thin Python binding of libsage_mi355x.so (C ABI in include/sage_mi355x.h).
+
+Argument marshalling only: every step of the attention runs in the library's
+HIP kernels.  torch supplies device memory and the current stream.  The
+library must have been built (``python -m quantized_softmax_attention_amd.build``);
+there is no fallback of any kind, and every non-zero status raises SageError.
+
+The functions carry the C names.  Tensor arguments are torch tensors on the GPU:
+bf16 inputs are [B, N, H, D] views with unit last stride (any batch/token/head
+strides, e.g. column slices of a packed [B, N, 3*H*D] projection buffer).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage_mi355x.so")
+
+HEAD_DIM = 128
+Q_BLOCK = 32
+K_BLOCK = 64
+P_TILE = 64
+N_ALIGN = 256
+
+STATUS = {0: "SAGE_OK", 1: "SAGE_ERR_NULL", 2: "SAGE_ERR_SHAPE", 3: "SAGE_ERR_STRIDE", 4: "SAGE_ERR_ALIGN",
+          5: "SAGE_ERR_WORKSPACE", 6: "SAGE_ERR_HIP", 7: "SAGE_ERR_VALUE"}
+
+
+class SageError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), sage_status_str(status)))
+
+
+class BF16In(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+class BF16Out(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_n", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libsage_mi355x.so is not built (run python -m quantized_softmax_attention_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, sz, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+        pin, pout = ctypes.POINTER(BF16In), ctypes.POINTER(BF16Out)
+        L.sage_npad.argtypes, L.sage_npad.restype = [i], ctypes.c_int64
+        L.sage_qk_workspace_bytes.argtypes, L.sage_qk_workspace_bytes.restype = [i, i, i, i], sz
+        L.sage_v_workspace_bytes.argtypes, L.sage_v_workspace_bytes.restype = [i, i, i, i], sz
+        L.sage_quantize_qk.argtypes = [pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sage_quantize_v.argtypes = [pin, i, i, i, i, vp, vp, vp, sz, vp]
+        L.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, pout, vp]
+        L.sage_attn_fwd_bf16.argtypes = [pin, pin, pin, i, i, i, i, f, pout, vp]
+        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_bf16"):
+            getattr(L, fn).restype = i
+        L.sage_status_str.argtypes, L.sage_status_str.restype = [i], ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def sage_status_str(status: int) -> str:
+    return lib().sage_status_str(int(status)).decode()
+
+
+def _check(status: int, fn: str) -> None:
+    if status != 0:
+        raise SageError(status, fn)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _shape(t: torch.Tensor):
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, N, H, D] view with unit last stride")
+    return tuple(t.shape)
+
+
+def bf16_in(t: torch.Tensor) -> BF16In:
+    _shape(t)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("expected bfloat16")
+    return BF16In(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def bf16_out(t: torch.Tensor) -> BF16Out:
+    _shape(t)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("expected bfloat16")
+    return BF16Out(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def sage_npad(N: int) -> int:
+    return int(lib().sage_npad(N))
+
+
+def sage_qk_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
+    return int(lib().sage_qk_workspace_bytes(B, N, H, D))
+
+
+def sage_v_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
+    return int(lib().sage_v_workspace_bytes(B, N, H, D))
+
+
+def sage_quantize_qk(q, k, q_codes, q_scale, k_codes, k_scale, k_mean, workspace, stream=None) -> None:
+    B, N, H, D = _shape(q)
+    qi, ki = bf16_in(q), bf16_in(k)
+    st = lib().sage_quantize_qk(ctypes.byref(qi), ctypes.byref(ki), B, N, H, D, _ptr(q_codes), _ptr(q_scale),
+                                _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sage_quantize_qk")
+
+
+def sage_quantize_v(v, v_codes, v_scale, workspace, stream=None) -> None:
+    B, N, H, D = _shape(v)
+    vi = bf16_in(v)
+    st = lib().sage_quantize_v(ctypes.byref(vi), B, N, H, D, _ptr(v_codes), _ptr(v_scale), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sage_quantize_v")
+
+
+def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, out, sm_scale=None, stream=None) -> None:
+    B, N, H, D = _shape(out)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    o = bf16_out(out)
+    st = lib().sage_attn_fwd(_ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes),
+                             _ptr(v_scale), B, N, H, D, float(sm_scale), ctypes.byref(o), _stream(stream))
+    _check(st, "sage_attn_fwd")
+
+
+def sage_attn_fwd_bf16(q, k, v, out, sm_scale=None, stream=None) -> None:
+    B, N, H, D = _shape(q)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    qi, ki, vi, o = bf16_in(q), bf16_in(k), bf16_in(v), bf16_out(out)
+    st = lib().sage_attn_fwd_bf16(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D,
+                                  float(sm_scale), ctypes.byref(o), _stream(stream))
+    _check(st, "sage_attn_fwd_bf16")
+
+
+class Buffers:
+    """Device buffers one quantised forward needs, allocated once with torch
+    (library-defined layouts: see the public header)."""
+
+    def __init__(self, B: int, N: int, H: int, device="cuda", D: int = HEAD_DIM):
+        npad = sage_npad(N)
+        self.B, self.N, self.H, self.D, self.npad = B, N, H, D, npad
+        dev = torch.device(device)
+        self.q_codes = torch.empty(B, H, npad, D, dtype=torch.int8, device=dev)
+        self.k_codes = torch.empty(B, H, npad, D, dtype=torch.int8, device=dev)
+        self.q_scale = torch.empty(B, H, npad // Q_BLOCK, dtype=torch.float32, device=dev)
+        self.k_scale = torch.empty(B, H, npad // K_BLOCK, dtype=torch.float32, device=dev)
+        self.k_mean = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+        self.v_codes = torch.empty(B, H, npad // P_TILE, D, P_TILE, dtype=torch.uint8, device=dev)
+        self.v_scale = torch.empty(B, H, D, dtype=torch.float32, device=dev)
+        self.ws_qk = torch.empty(max(1, sage_qk_workspace_bytes(B, N, H, D) // 8), dtype=torch.float64, device=dev)
+        self.ws_v = torch.empty(max(1, sage_v_workspace_bytes(B, N, H, D) // 4), dtype=torch.float32, device=dev)
+
+
+def quantize(q, k, v, buf: Buffers, stream=None) -> None:
+    """qk_quantize (with K smoothing) then v_quantize into `buf`."""
+    sage_quantize_qk(q, k, buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.k_mean, buf.ws_qk, stream)
+    sage_quantize_v(v, buf.v_codes, buf.v_scale, buf.ws_v, stream)
+
+
+def forward(q, k, v, out, buf: Buffers, sm_scale=None, stream=None) -> None:
+    """The quantised forward: quantize Q/K/V, then the fused attention into `out`."""
+    quantize(q, k, v, buf, stream)
+    sage_attn_fwd(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, out, sm_scale, stream)
+
+
+def token_major_out(B: int, N: int, H: int, device="cuda", D: int = HEAD_DIM) -> torch.Tensor:
+    """A [B, N, H*D] bf16 output viewed as [B, N, H, D]."""
+    return torch.empty(B, N, H * D, dtype=torch.bfloat16, device=device).view(B, N, H, D)
+
+
+def v_token_order() -> torch.Tensor:
+    """kappa: the token (within a 64-key tile) held at byte p of a V-code row."""
+    p = torch.arange(P_TILE)
+    u, j = p // 32, p % 32
+    return 32 * (j // 16) + 8 * ((j % 16) // 4) + 4 * u + (j % 4)

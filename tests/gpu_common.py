@@ -1,0 +1,120 @@
+"""Helpers for the GPU parity tests: run the library through its C ABI, bring
+results back, and compute (cached) oracle references for the same seeded
+inputs.  Oracle inputs are always the seeded CPU tensors, never GPU output."""
+import functools
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from quantized_softmax_attention_amd import inputs, sage
+from tests.helpers import oracle_view
+
+SM = 1.0 / math.sqrt(128.0)
+
+
+def kappa():
+    """Token (within a 64-key tile) of byte p of a V-code row, as the public
+    header defines it: p = 32u + j -> 32*(j/16) + 8*((j%16)/4) + 4u + j%4."""
+    p = np.arange(64)
+    u, j = p // 32, p % 32
+    return 32 * (j // 16) + 8 * ((j % 16) // 4) + 4 * u + (j % 4)
+
+
+def unpermute_v(vc_tiles: np.ndarray, N: int) -> np.ndarray:
+    """[B, H, T, D, 64] tile-major codes -> logical [B, H, N, D] (plus a check
+    that the padding tokens are zero)."""
+    B, H, T, D, P = vc_tiles.shape
+    logical = np.empty((B, H, T * 64, D), np.uint8)
+    k = kappa()
+    for p in range(64):
+        logical[:, :, k[p]::64, :] = vc_tiles[:, :, :, :, p]
+    assert not logical[:, :, N:].any(), "padding tokens must hold 0x00"
+    return logical[:, :, :N]
+
+
+def gpu_case(case: inputs.Case) -> inputs.Case:
+    return case.to("cuda")
+
+
+def run_quant(gcase: inputs.Case):
+    """Quantise on the GPU; return numpy copies of every output buffer."""
+    buf = sage.Buffers(gcase.B, gcase.N, gcase.H)
+    sage.quantize(gcase.q, gcase.k, gcase.v, buf)
+    torch.cuda.synchronize()
+    return buf
+
+
+def run_attn(gcase: inputs.Case, buf=None):
+    if buf is None:
+        buf = run_quant(gcase)
+    out = sage.token_major_out(gcase.B, gcase.N, gcase.H)
+    sage.sage_attn_fwd(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, out, SM)
+    torch.cuda.synchronize()
+    return out, buf
+
+
+def run_attn_bf16(gcase: inputs.Case):
+    out = sage.token_major_out(gcase.B, gcase.N, gcase.H)
+    sage.sage_attn_fwd_bf16(gcase.q, gcase.k, gcase.v, out, SM)
+    torch.cuda.synchronize()
+    return out
+
+
+def out_rows(out: torch.Tensor, rows: np.ndarray) -> np.ndarray:
+    """[B, N, H, D] output -> [B, H, R, D] float64 at the sampled rows."""
+    o = out.float().cpu().numpy()
+    B, N, H, D = o.shape
+    res = np.empty((B, H, rows.shape[2], D))
+    for b in range(B):
+        for h in range(H):
+            res[b, h] = o[b, rows[b, h], h]
+    return res
+
+
+class OracleRef:
+    """Oracle results for one seeded CPU case (quantisation at full size;
+    attention on the requested rows)."""
+
+    def __init__(self, case: inputs.Case):
+        self.case = case
+        self.q, self.k, self.v = (oracle_view(t) for t in (case.q, case.k, case.v))
+
+    @functools.cached_property
+    def km(self):
+        return oracle.kmean(self.k)
+
+    @functools.cached_property
+    def qq(self):
+        return oracle.quant_q(self.q, 32)
+
+    @functools.cached_property
+    def kq(self):
+        return oracle.quant_k(self.k, self.km, 64)
+
+    @functools.cached_property
+    def vq(self):
+        return oracle.quant_v(self.v)
+
+    def exact(self, rows):
+        return oracle.attn_exact(self.q, self.k, self.v, SM, rows)
+
+    def method(self, rows):
+        (qc, qs), (kc, ks), (vc, vs) = self.qq, self.kq, self.vq
+        return oracle.attn_method(qc, qs, kc, ks, vc, vs, SM, rows)
+
+
+@functools.lru_cache(maxsize=5)
+def config_ref(name: str) -> OracleRef:
+    return OracleRef(inputs.config(name))
+
+
+def rel_l2(a, b) -> float:
+    return oracle.rel_l2(a, b)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """The library's output rounding (bf16, nearest even) applied to an fp64
+    oracle result, so that GPU bf16 outputs compare against the same definition."""
+    return torch.from_numpy(np.ascontiguousarray(x, np.float64)).float().to(torch.bfloat16).double().numpy()

@@ -1,0 +1,84 @@
+"""Quantiser parity on the GPU through the C ABI: K mean, Q/K INT8 codes and
+scales, V E4M3 codes and scales must equal the oracle's bit for bit, at the
+five workloads' shapes (full size) and at ragged edge shapes."""
+import numpy as np
+import pytest
+import torch
+
+from quantized_softmax_attention_amd import inputs, sage
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_bitexact(case: inputs.Case, ref: G.OracleRef):
+    B, N, H = case.B, case.N, case.H
+    buf = G.run_quant(G.gpu_case(case))
+    npad = sage.sage_npad(N)
+    nq, nk = -(-N // 32), -(-N // 64)
+    km = buf.k_mean.cpu().numpy()
+    assert np.array_equal(km.view(np.uint32), ref.km.view(np.uint32)), "k_mean"
+    qc, qs = buf.q_codes.cpu().numpy(), buf.q_scale.cpu().numpy()
+    kc, ks = buf.k_codes.cpu().numpy(), buf.k_scale.cpu().numpy()
+    (rqc, rqs), (rkc, rks) = ref.qq, ref.kq
+    assert np.array_equal(qc[:, :, :N], rqc), "q_codes"
+    assert np.array_equal(kc[:, :, :N], rkc), "k_codes"
+    assert not qc[:, :, N:].any() and not kc[:, :, N:].any(), "padding codes"
+    assert np.array_equal(qs[:, :, :nq].view(np.uint32), rqs.view(np.uint32)), "q_scale"
+    assert np.array_equal(ks[:, :, :nk].view(np.uint32), rks.view(np.uint32)), "k_scale"
+    assert not qs[:, :, nq:].any() and not ks[:, :, nk:].any(), "padding scales"
+    assert qs.shape == (B, H, npad // 32) and ks.shape == (B, H, npad // 64)
+    vc = G.unpermute_v(buf.v_codes.cpu().numpy(), N)
+    rvc, rvs = ref.vq
+    assert np.array_equal(buf.v_scale.cpu().numpy().view(np.uint32), rvs.view(np.uint32)), "v_scale"
+    assert np.array_equal(vc, rvc), "v_codes"
+
+
+def test_kappa_matches_binding():
+    assert np.array_equal(G.kappa(), sage.v_token_order().numpy())
+    assert sorted(G.kappa()) == list(range(64))
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "block24", "stress"])
+def test_quantizers_bitexact_workloads(name):
+    print("quantizer parity:", name, flush=True)
+    ref = G.config_ref(name)
+    _check_bitexact(ref.case, ref)
+
+
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 63, 64, 65, 127, 129, 255, 257, 4095])
+def test_quantizers_bitexact_ragged(N):
+    print("quantizer parity ragged N =", N, flush=True)
+    case = inputs.packed_case(2, N, 3, seed=N, stress=(N % 2 == 1))
+    _check_bitexact(case, G.OracleRef(case))
+
+
+def test_quantizers_hnd_and_packed_layouts_agree():
+    case = inputs.packed_case(1, 300, 4, seed=7)
+    hnd = inputs.Case("hnd", 1, 300, 4, 128, *(t.transpose(1, 2).contiguous().transpose(1, 2)
+                                               for t in (case.q, case.k, case.v)))
+    a, b = G.run_quant(G.gpu_case(case)), G.run_quant(G.gpu_case(hnd))
+    for name in ("q_codes", "q_scale", "k_codes", "k_scale", "k_mean", "v_codes", "v_scale"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_quantizers_special_values():
+    # zero blocks, a constant K channel, a zero V channel, ties, tiny and large values
+    B, N, H, D = 1, 200, 2, 128
+    x = torch.zeros(B, N, H, D)
+    x[0, :, 0, 5] = 3.0                                   # constant K channel -> code 0
+    x[0, 40:, 1] = torch.linspace(-1000, 1000, (N - 40) * D).reshape(N - 40, D)
+    x[0, 7, 1, 9] = 2.0 ** -120                           # tiny
+    q = x.clone(); q[0, 64:96] = 0                        # an all-zero Q block
+    v = x.clone(); v[0, :, 0, 11] = 0                     # an all-zero V channel
+    v[0, 3, 0, 12] = -(2.0 ** -30)
+    case = inputs.Case("special", B, N, H, D, q.to(torch.bfloat16), x.to(torch.bfloat16), v.to(torch.bfloat16))
+    _check_bitexact(case, G.OracleRef(case))
+
+
+def test_quantizers_repeatable():
+    case = inputs.config("tiny")
+    g = G.gpu_case(case)
+    a, b = G.run_quant(g), G.run_quant(g)
+    for name in ("q_codes", "q_scale", "k_codes", "k_scale", "k_mean", "v_codes", "v_scale"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
