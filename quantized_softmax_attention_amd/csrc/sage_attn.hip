@@ -59,92 +59,89 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-struct Prefetch {
-    v4i k0, k1, v0, v1;
-};
+// Direct HBM -> LDS staging (global_load_lds_dwordx4): lane L of a wave's load
+// instruction writes LDS bytes [16 L, 16 L + 16) after the instruction's base, so
+// each lane fetches the global chunk that belongs at its (swizzled) LDS slot.
+// Wave w issues slots [128 w, 128 w + 128) of each 512-slot tile.
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void load_tile(Prefetch &p, const int8_t *ktile, const uint8_t *vtile, int t) {
-    p.k0 = reinterpret_cast<const v4i *>(ktile)[t];
-    p.k1 = reinterpret_cast<const v4i *>(ktile)[t + kThreads];
-    p.v0 = reinterpret_cast<const v4i *>(vtile)[t];
-    p.v1 = reinterpret_cast<const v4i *>(vtile)[t + kThreads];
-}
-
-__device__ __forceinline__ void store_tile(const Prefetch &p, v4i *lk, v4i *lv, int t) {
-    int g0 = t, g1 = t + kThreads;
-    lk[k_slot(g0 >> 3, g0 & 7)] = p.k0;
-    lk[k_slot(g1 >> 3, g1 & 7)] = p.k1;
-    lv[v_slot(g0 >> 2, g0 & 3)] = p.v0;
-    lv[v_slot(g1 >> 2, g1 & 3)] = p.v1;
-}
-
-// One 64-key step for one wave.  TAIL masks keys >= nvalid (last tile only).
-template <bool TAIL>
-__device__ __forceinline__ void tile_step(const v4i *lk, const v4i *lv, const v4i (&qa)[4], float cq,
-                                          float ksc, int nvalid, int hl, int ql, float &m2, float &lsum,
-                                          v16f (&o)[4]) {
-    // S^T = K Q^T: two 32-key blocks, four 32-channel k-steps each.
-    v16i s[2];
+__device__ __forceinline__ void lds_load_k(v4i *lk, const int8_t *tile, int w, int lane) {
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-        s[kb] = v16i{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int st = 0; st < 4; st++) {
-            v4i ka = lk[k_slot(32 * kb + ql, 2 * st + hl)];
-            s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qa[st], s[kb], 0, 0, 0);
-        }
+    for (int i = 0; i < 2; i++) {
+        const int slot = 128 * w + 64 * i + lane;
+        const int r = slot >> 3, cs = slot & 7;                 // LDS slot -> (row, stored chunk)
+        const int c = cs ^ ((r ^ (r >> 3)) & 7);                // stored chunk -> source chunk
+        __builtin_amdgcn_global_load_lds(tile + r * 128 + c * 16, (lds_void *)(lk + 128 * w + 64 * i), 16, 0, 0);
     }
-    // Lane (hl, ql) register r of block kb holds key 32*kb + 8*(r/4) + 4*hl + r%4.
+}
+__device__ __forceinline__ void lds_load_v(v4i *lv, const uint8_t *tile, int w, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int slot = 128 * w + 64 * i + lane;
+        const int d = slot >> 2, cs = slot & 3;
+        const int c = cs ^ (((d >> 1) ^ (d >> 3)) & 3);
+        __builtin_amdgcn_global_load_lds(tile + d * 64 + c * 16, (lds_void *)(lv + 128 * w + 64 * i), 16, 0, 0);
+    }
+}
+// Wait for this wave's outstanding HBM -> LDS loads (vmcnt = 0), then the barrier.
+__device__ __forceinline__ void wait_lds_loads_and_sync() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
+    __syncthreads();
+}
+
+// S^T = K Q^T for one 64-key tile: two 32-key blocks, four 32-channel k-steps.
+// Lane (hl, ql) register r of block kb holds key 32*kb + 8*(r/4) + 4*hl + r%4.
+// MFMA i (0..7) is block i/4, k-step i%4.
+__device__ __forceinline__ void qk_mfma(const v4i *lk, const v4i (&qa)[4], int hl, int ql, v16i (&s)[2], int i) {
+    const int kb = i >> 2, st = i & 3;
+    v4i ka = lk[k_slot(32 * kb + ql, 2 * st + hl)];
+    s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qa[st], st ? s[kb] : v16i{}, 0, 0, 0);
+}
+
+__device__ __forceinline__ void qk_tile(const v4i *lk, const v4i (&qa)[4], int hl, int ql, v16i (&s)[2]) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) qk_mfma(lk, qa, hl, ql, s, i);
+}
+
+// Running maximum after one tile, from its int32 scores (log2 units; c2 >= 0 so
+// the maximum of c2 * a is c2 * max a).  TAIL first masks keys >= nvalid.
+template <bool TAIL>
+__device__ __forceinline__ float tile_max(v16i (&s)[2], float c2, int nvalid, int hl, float m2) {
     if (TAIL) {
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (key >= nvalid) s[kb][r] = INT32_MIN;
-            }
+            for (int r = 0; r < 16; r++)
+                if (32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3) >= nvalid) s[kb][r] = INT32_MIN;
     }
-    int imax = INT32_MIN;
+    int imax = max(s[0][0], s[0][1]);
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+    for (int r = 2; r < 16; r += 2) imax = max(imax, max(s[0][r], s[0][r + 1]));
 #pragma unroll
-        for (int r = 0; r < 16; r++) imax = max(imax, s[kb][r]);
+    for (int r = 0; r < 16; r += 2) imax = max(imax, max(s[1][r], s[1][r + 1]));
     imax = pair_max(imax);
+    return fmaxf(m2, c2 * (float)imax);
+}
 
-    const float c2 = cq * ksc;                       // log2-domain scale of this step
-    const float mnew = fmaxf(m2, c2 * (float)imax);  // c2 >= 0: monotone in a
-    const float alpha = fast_exp2(m2 - mnew);        // 0 on the first step
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // wave-uniform; skip when no max moved
-        lsum *= alpha;
+// p' = 448 * exp(s - m) for registers 4c..4c+3 of the tile (c = 0..7), summed
+// in fp32 before rounding, packed to E4M3 into operand dword c.
+template <bool TAIL>
+__device__ __forceinline__ void tile_exp_chunk(const v16i (&s)[2], float c2, float bias, int nvalid, int hl, int c,
+                                               v8i &pf, float &part) {
+    const int kb = c >> 2, r = 4 * (c & 3);
+    float p[4];
 #pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) o[db][r] *= alpha;
+    for (int i = 0; i < 4; i++) {
+        p[i] = fast_exp2(c2 * (float)s[kb][r + i] - bias);
+        if (TAIL && 32 * kb + 8 * (r >> 2) + 4 * hl + i >= nvalid) p[i] = 0.0f;
     }
-    m2 = mnew;
-    const float bias = mnew - kLog2_448;
+    part += (p[0] + p[1]) + (p[2] + p[3]);
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
+    pf[c] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
+}
 
-    // p' = 448 * exp(s - m) in fp32; sum before rounding; pack to E4M3.
-    v8i pf;
-    float part = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int r = 0; r < 16; r += 4) {
-            // registers r..r+3 -> operand bytes j = 16*kb + r .. +3 (one dword)
-            float p[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                p[i] = fast_exp2(c2 * (float)s[kb][r + i] - bias);
-                if (TAIL && 32 * kb + 8 * (r >> 2) + 4 * hl + i >= nvalid) p[i] = 0.0f;
-            }
-            part += (p[0] + p[1]) + (p[2] + p[3]);
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-            pf[(16 * kb + r) >> 2] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
-        }
-    lsum += part;
-
-    // O^T += V^T P^T, 32 channels per MFMA.
+// O^T += V^T P^T, 32 channels per MFMA.
+__device__ __forceinline__ void pv_tile(const v4i *lv, const v8i &pf, int hl, int ql, v16f (&o)[4]) {
 #pragma unroll
     for (int db = 0; db < 4; db++) {
         const int d = 32 * db + ql;
@@ -155,11 +152,62 @@ __device__ __forceinline__ void tile_step(const v4i *lk, const v4i *lv, const v4
     }
 }
 
+__device__ __forceinline__ void rescale(float alpha, v16f (&o)[4]) {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // wave-uniform; skip when no max moved
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) o[db][r] *= alpha;
+    }
+}
+
+// Per-wave running state of the online softmax.
+struct RowState {
+    float m2;     // running maximum, log2 units
+    float lsum;   // running sum of p' over this lane's keys
+    float alpha;  // rescale factor of the last processed tile, not yet applied to O
+    v8i pf;       // E4M3 P^T operand of the last processed tile
+};
+
+// Step t of the software pipeline, one scheduling region after the rescale
+// branch:
+//   1. (PV)   O = alpha(t-1) * O  (branch, rarely taken), then O += V(t-1) P(t-1)
+//   2.        running max over tile t; alpha(t); l = alpha(t) * l + sum p'(t)
+//   3.        p'(t) -> E4M3, with the 8 QK^T MFMAs of tile t+1 (QK) interleaved
+// The LDS holds V(t-1) in lv_prev and K(t+1) in lk_next.
+template <bool PV, bool QK, bool TAIL>
+__device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_next, const v4i *lv_prev,
+                                     const v4i (&qa)[4], float c2, int nvalid, int hl, int ql, RowState &st,
+                                     v16f (&o)[4]) {
+    if (PV) {
+        rescale(st.alpha, o);
+        pv_tile(lv_prev, st.pf, hl, ql, o);
+    }
+    const float mnew = tile_max<TAIL>(s, c2, nvalid, hl, st.m2);
+    st.alpha = fast_exp2(st.m2 - mnew);        // 0 on the first tile (m2 = -inf)
+    st.m2 = mnew;
+    const float bias = mnew - kLog2_448;
+    float part = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; c++) {
+        if (QK) qk_mfma(lk_next, qa, hl, ql, sn, c);
+        tile_exp_chunk<TAIL>(s, c2, bias, nvalid, hl, c, st.pf, part);
+    }
+    st.lsum = st.lsum * st.alpha + part;
+}
+
+// Software pipeline per wave: while the softmax of tile t runs on the VALU, the
+// QK^T MFMAs of tile t+1 and the P.V MFMAs of tile t-1 are in flight.  K tiles
+// are staged two steps ahead of the softmax and V tiles one behind: step t
+// reads K(t+1), V(t-1) from LDS and writes K(t+2), V(t) (loaded from HBM at the
+// start of the step) into the buffers of K(t), V(t-2).
 __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
     const int8_t *__restrict__ qc, const float *__restrict__ qs, const int8_t *__restrict__ kc,
     const float *__restrict__ ks, const uint8_t *__restrict__ vc, const float *__restrict__ vs, int N,
     int H, int64_t Npad, float c_base, OutView out, int nqwg) {
-    __shared__ v4i lds[2][2][kChunks];   // [buffer][K, V][chunk]
+    // four separate LDS objects, always selected at compile time, so the
+    // compiler can tell the buffers being read from the ones being filled
+    __shared__ v4i lk0[kChunks], lk1[kChunks], lv0[kChunks], lv1[kChunks];
 
     const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
     const int qb = (int)(id % (uint32_t)nqwg);
@@ -180,30 +228,76 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
 
     const int ntiles = (N + kTile - 1) / kTile;
     const int tail_valid = N - (ntiles - 1) * kTile;
+    const bool partial = tail_valid != kTile;
 
     v16f o[4];
 #pragma unroll
     for (int db = 0; db < 4; db++)
         o[db] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    float m2 = -INFINITY, lsum = 0.0f;
+    RowState rs{-INFINITY, 0.0f, 1.0f, v8i{}};
 
-    Prefetch pre;
-    load_tile(pre, kbase, vbase, t);
-    store_tile(pre, lds[0][0], lds[0][1], t);
+    // prologue: K(0), K(1) into LDS; S(0) = K(0) Q^T; K(0)'s buffer is
+    // rewritten in step 0, so every wave finishes reading it first.
+    lds_load_k(lk0, kbase, w, lane);
+    if (ntiles > 1) lds_load_k(lk1, kbase + kTileBytes, w, lane);
+    wait_lds_loads_and_sync();
+    v16i sa[2], sb[2];
+    qk_tile(lk0, qa, hl, ql, sa);
     __syncthreads();
 
-    for (int tt = 0; tt < ntiles; tt++) {
-        const int buf = tt & 1;
-        const bool more = tt + 1 < ntiles;
-        if (more) load_tile(pre, kbase + (int64_t)(tt + 1) * kTileBytes, vbase + (int64_t)(tt + 1) * kTileBytes, t);
-        const float ksc = ksb[tt];
-        if (tt + 1 < ntiles || tail_valid == kTile)
-            tile_step<false>(lds[buf][0], lds[buf][1], qa, cq, ksc, kTile, hl, ql, m2, lsum, o);
-        else
-            tile_step<true>(lds[buf][0], lds[buf][1], qa, cq, ksc, tail_valid, hl, ql, m2, lsum, o);
-        if (more) store_tile(pre, lds[buf ^ 1][0], lds[buf ^ 1][1], t);
-        __syncthreads();
+    // Step t stages K(t+2) and V(t) into the buffers of K(t) and V(t-2), which
+    // the previous step finished reading before its barrier.  Buffer parity is
+    // t's: even steps fill lk0/lv0 and read lk1/lv1, odd steps the reverse.
+    auto prefetch = [&](int tt, v4i *lkw, v4i *lvw) {
+        if (tt + 2 < ntiles) lds_load_k(lkw, kbase + (int64_t)(tt + 2) * kTileBytes, w, lane);
+        lds_load_v(lvw, vbase + (int64_t)tt * kTileBytes, w, lane);
+    };
+
+    // step 0 (no P.V yet)
+    prefetch(0, lk0, lv0);
+    if (ntiles == 1) {
+        if (partial) step<false, false, true>(sa, sb, lk1, lv1, qa, cq * ksb[0], tail_valid, hl, ql, rs, o);
+        else step<false, false, false>(sa, sb, lk1, lv1, qa, cq * ksb[0], kTile, hl, ql, rs, o);
+    } else {
+        step<false, true, false>(sa, sb, lk1, lv1, qa, cq * ksb[0], kTile, hl, ql, rs, o);
     }
+    wait_lds_loads_and_sync();
+    // steps 1 .. ntiles-2, two per iteration (odd then even) so the score
+    // registers and LDS buffers alternate statically
+    int tt = 1;
+    for (; tt + 2 < ntiles; tt += 2) {
+        prefetch(tt, lk1, lv1);
+        step<true, true, false>(sb, sa, lk0, lv0, qa, cq * ksb[tt], kTile, hl, ql, rs, o);
+        wait_lds_loads_and_sync();
+        prefetch(tt + 1, lk0, lv0);
+        step<true, true, false>(sa, sb, lk1, lv1, qa, cq * ksb[tt + 1], kTile, hl, ql, rs, o);
+        wait_lds_loads_and_sync();
+    }
+    if (tt + 1 < ntiles) {   // one more full odd step: scores in sb
+        prefetch(tt, lk1, lv1);
+        step<true, true, false>(sb, sa, lk0, lv0, qa, cq * ksb[tt], kTile, hl, ql, rs, o);
+        wait_lds_loads_and_sync();
+        tt++;
+    }
+    // last step tt = ntiles - 1 (if >= 1): odd -> scores in sb, reads lv0; even -> sa, lv1
+    if (tt < ntiles) {
+        const float c2 = cq * ksb[tt];
+        if (tt & 1) {
+            prefetch(tt, lk1, lv1);
+            if (partial) step<true, false, true>(sb, sa, lk0, lv0, qa, c2, tail_valid, hl, ql, rs, o);
+            else step<true, false, false>(sb, sa, lk0, lv0, qa, c2, kTile, hl, ql, rs, o);
+        } else {
+            prefetch(tt, lk0, lv0);
+            if (partial) step<true, false, true>(sa, sb, lk1, lv1, qa, c2, tail_valid, hl, ql, rs, o);
+            else step<true, false, false>(sa, sb, lk1, lv1, qa, c2, kTile, hl, ql, rs, o);
+        }
+        wait_lds_loads_and_sync();
+    }
+    // drain: P.V of the last tile (V(ntiles-1) sits in the buffer of its parity)
+    rescale(rs.alpha, o);
+    if ((ntiles - 1) & 1) pv_tile(lv1, rs.pf, hl, ql, o);
+    else pv_tile(lv0, rs.pf, hl, ql, o);
+    const float lsum = rs.lsum;
 
     // Epilogue: the two lanes of a query hold different keys' partial sums.
     const float ltot = pair_sum(lsum);
