@@ -39,10 +39,15 @@ constexpr int kChunks = kTileBytes / 16;   // 512 16-byte chunks per tile
 constexpr float kLog2E = 1.4426950408889634f;
 constexpr float kLog2_448 = 8.807354922057604f;
 
-// LDS slot of 16-byte chunk c (0..7) of K row r (0..63).
+// LDS slot of 16-byte chunk c (0..7) of K row r (0..63) (conflict-free for the
+// fragment reads: 32 rows x one chunk).
 __device__ __forceinline__ int k_slot(int r, int c) { return r * 8 + (c ^ ((r ^ (r >> 3)) & 7)); }
-// LDS slot of 16-byte chunk c (0..3) of V channel row d (0..127).
-__device__ __forceinline__ int v_slot(int d, int c) { return d * 4 + (c ^ (((d >> 1) ^ (d >> 3)) & 3)); }
+// LDS slot of 16-byte chunk c (0..3) of V channel row d (0..127).  ds_read_b128
+// serves 16 consecutive lanes per cycle from 64 four-byte banks; with this XOR
+// the 32 channel rows x 2 chunks a fragment read touches are conflict-free
+// (measured: 4 LDS cycles per read, the minimum).
+__device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
+__device__ __forceinline__ int v_slot(int d, int c) { return d * 4 + (c ^ v_swz(d)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -59,41 +64,64 @@ __device__ __forceinline__ float pair_sum(float x) {
     return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
-// Direct HBM -> LDS staging (global_load_lds_dwordx4): lane L of a wave's load
-// instruction writes LDS bytes [16 L, 16 L + 16) after the instruction's base, so
-// each lane fetches the global chunk that belongs at its (swizzled) LDS slot.
-// Wave w issues slots [128 w, 128 w + 128) of each 512-slot tile.
+// Direct HBM -> LDS staging (buffer_load_dwordx4 ... lds): lane L of a wave's
+// load instruction writes LDS bytes [16 L, 16 L + 16) after the instruction's
+// LDS base, so each lane fetches the global chunk that belongs at its
+// (swizzled) LDS slot.  Wave w issues slots [128 w, 128 w + 128) of each
+// 512-slot tile.  The per-lane byte offsets are loop invariant; the tile base
+// lives in a buffer descriptor (scalar registers) whose 8 KB record limit also
+// bounds every access to the tile.
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void lds_load_k(v4i *lk, const int8_t *tile, int w, int lane) {
+struct TileLoader {
+    int koff[2], voff[2];   // per-lane source byte offsets within a K tile and a V tile
+};
+
+__device__ __forceinline__ TileLoader make_loader(int w, int lane) {
+    TileLoader L;
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int slot = 128 * w + 64 * i + lane;
-        const int r = slot >> 3, cs = slot & 7;                 // LDS slot -> (row, stored chunk)
-        const int c = cs ^ ((r ^ (r >> 3)) & 7);                // stored chunk -> source chunk
-        __builtin_amdgcn_global_load_lds(tile + r * 128 + c * 16, (lds_void *)(lk + 128 * w + 64 * i), 16, 0, 0);
+        const int r = slot >> 3, rc = slot & 7;                  // K: LDS slot -> row, stored chunk
+        L.koff[i] = r * 128 + 16 * (rc ^ ((r ^ (r >> 3)) & 7));
+        const int d = slot >> 2, dc = slot & 3;                  // V: LDS slot -> channel, stored chunk
+        L.voff[i] = d * 64 + 16 * (dc ^ v_swz(d));
     }
+    return L;
 }
-__device__ __forceinline__ void lds_load_v(v4i *lv, const uint8_t *tile, int w, int lane) {
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *tile) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(tile), 0, kTileBytes, 0x00020000);
+}
+
+__device__ __forceinline__ void lds_load_k(v4i *lk, const int8_t *tile, const TileLoader &L, int w) {
+    const auto r = tile_rsrc(tile);
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-        const int slot = 128 * w + 64 * i + lane;
-        const int d = slot >> 2, cs = slot & 3;
-        const int c = cs ^ (((d >> 1) ^ (d >> 3)) & 3);
-        __builtin_amdgcn_global_load_lds(tile + d * 64 + c * 16, (lds_void *)(lv + 128 * w + 64 * i), 16, 0, 0);
-    }
+    for (int i = 0; i < 2; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lk + 128 * w + 64 * i), 16, L.koff[i], 0, 0, 0);
 }
-// Wait for this wave's outstanding HBM -> LDS loads (vmcnt = 0), then the barrier.
+__device__ __forceinline__ void lds_load_v(v4i *lv, const uint8_t *tile, const TileLoader &L, int w) {
+    const auto r = tile_rsrc(tile);
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lv + 128 * w + 64 * i), 16, L.voff[i], 0, 0, 0);
+}
+// Wait for this wave's outstanding HBM -> LDS loads (vmcnt = 0), then the
+// barrier.  The scheduling fences keep register-only work of neighbouring steps
+// from drifting across it, so each step keeps its MFMA/VALU interleave.
 __device__ __forceinline__ void wait_lds_loads_and_sync() {
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // S^T = K Q^T for one 64-key tile: two 32-key blocks, four 32-channel k-steps.
 // Lane (hl, ql) register r of block kb holds key 32*kb + 8*(r/4) + 4*hl + r%4.
-// MFMA i (0..7) is block i/4, k-step i%4.
+// MFMA i (0..7) is block i%2, k-step i/2: the two accumulation chains
+// alternate, so no MFMA waits on the one issued just before it.
 __device__ __forceinline__ void qk_mfma(const v4i *lk, const v4i (&qa)[4], int hl, int ql, v16i (&s)[2], int i) {
-    const int kb = i >> 2, st = i & 3;
+    const int kb = i & 1, st = i >> 1;
     v4i ka = lk[k_slot(32 * kb + ql, 2 * st + hl)];
     s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qa[st], st ? s[kb] : v16i{}, 0, 0, 0);
 }
@@ -114,11 +142,14 @@ __device__ __forceinline__ float tile_max(v16i (&s)[2], float c2, int nvalid, in
             for (int r = 0; r < 16; r++)
                 if (32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3) >= nvalid) s[kb][r] = INT32_MIN;
     }
-    int imax = max(s[0][0], s[0][1]);
+    // a chain of 3-input maxima: 16 v_max3_i32 for 32 values
+    int imax = max(max(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-    for (int r = 2; r < 16; r += 2) imax = max(imax, max(s[0][r], s[0][r + 1]));
+    for (int r = 3; r < 15; r += 2) imax = max(max(imax, s[0][r]), s[0][r + 1]);
+    imax = max(max(imax, s[0][15]), s[1][0]);
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) imax = max(imax, max(s[1][r], s[1][r + 1]));
+    for (int r = 1; r < 15; r += 2) imax = max(max(imax, s[1][r]), s[1][r + 1]);
+    imax = max(imax, s[1][15]);
     imax = pair_max(imax);
     return fmaxf(m2, c2 * (float)imax);
 }
@@ -136,7 +167,9 @@ __device__ __forceinline__ void tile_exp_chunk(const v16i (&s)[2], float c2, flo
         if (TAIL && 32 * kb + 8 * (r >> 2) + 4 * hl + i >= nvalid) p[i] = 0.0f;
     }
     part += (p[0] + p[1]) + (p[2] + p[3]);
-    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
+    // the low and then the high half of the dword; the previous tile's value
+    // serves as the (fully overwritten) old operand, so no copy is needed
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[c], false);
     pf[c] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
 }
 
@@ -165,26 +198,23 @@ __device__ __forceinline__ void rescale(float alpha, v16f (&o)[4]) {
 struct RowState {
     float m2;     // running maximum, log2 units
     float lsum;   // running sum of p' over this lane's keys
-    float alpha;  // rescale factor of the last processed tile, not yet applied to O
-    v8i pf;       // E4M3 P^T operand of the last processed tile
+    v8i pf;       // E4M3 P^T operand of the last processed tile (its P.V is pending)
 };
 
-// Step t of the software pipeline, one scheduling region after the rescale
-// branch:
-//   1. (PV)   O = alpha(t-1) * O  (branch, rarely taken), then O += V(t-1) P(t-1)
+// Step t of the software pipeline, one scheduling region:
+//   1. (PV)   O += V(t-1) P(t-1), where O already carries alpha(t-1)
 //   2.        running max over tile t; alpha(t); l = alpha(t) * l + sum p'(t)
 //   3.        p'(t) -> E4M3, with the 8 QK^T MFMAs of tile t+1 (QK) interleaved
+//   4. (PV)   O = alpha(t) * O (a branch, taken only when some row's max moved;
+//             by then the P.V MFMAs of step 1 have completed)
 // The LDS holds V(t-1) in lv_prev and K(t+1) in lk_next.
 template <bool PV, bool QK, bool TAIL>
 __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_next, const v4i *lv_prev,
                                      const v4i (&qa)[4], float c2, int nvalid, int hl, int ql, RowState &st,
                                      v16f (&o)[4]) {
-    if (PV) {
-        rescale(st.alpha, o);
-        pv_tile(lv_prev, st.pf, hl, ql, o);
-    }
+    if (PV) pv_tile(lv_prev, st.pf, hl, ql, o);   // O = alpha(t-1) acc(t-2) + P(t-1) V(t-1)
     const float mnew = tile_max<TAIL>(s, c2, nvalid, hl, st.m2);
-    st.alpha = fast_exp2(st.m2 - mnew);        // 0 on the first tile (m2 = -inf)
+    const float alpha = fast_exp2(st.m2 - mnew);   // 0 on the first tile (m2 = -inf)
     st.m2 = mnew;
     const float bias = mnew - kLog2_448;
     float part = 0.0f;
@@ -193,7 +223,32 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
         if (QK) qk_mfma(lk_next, qa, hl, ql, sn, c);
         tile_exp_chunk<TAIL>(s, c2, bias, nvalid, hl, c, st.pf, part);
     }
-    st.lsum = st.lsum * st.alpha + part;
+    // Issue order for the region: the P.V MFMAs spread over the max reduction,
+    // then one QK^T MFMA (with its LDS read) per exp chunk.
+    if (PV) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads (V operand)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU
+        }
+    }
+    if (QK) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read (K operand)
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
+        }
+    }
+    // Everything above is consumed only in the next step, after the rescale
+    // branch; this empty statement reads it here so no pass sinks the work
+    // (or the MFMAs) out of this step's schedule.
+    asm volatile("" ::"v"(st.pf), "v"(part));
+    if (QK) asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    st.lsum = st.lsum * alpha + part;
+    if (PV) rescale(alpha, o);                    // O = alpha(t) acc(t-1); O is 0 before step 1
 }
 
 // Software pipeline per wave: while the softmax of tile t runs on the VALU, the
@@ -234,12 +289,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
 #pragma unroll
     for (int db = 0; db < 4; db++)
         o[db] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    RowState rs{-INFINITY, 0.0f, 1.0f, v8i{}};
+    RowState rs{-INFINITY, 0.0f, v8i{}};
 
     // prologue: K(0), K(1) into LDS; S(0) = K(0) Q^T; K(0)'s buffer is
     // rewritten in step 0, so every wave finishes reading it first.
-    lds_load_k(lk0, kbase, w, lane);
-    if (ntiles > 1) lds_load_k(lk1, kbase + kTileBytes, w, lane);
+    const TileLoader ldr = make_loader(w, lane);
+    lds_load_k(lk0, kbase, ldr, w);
+    if (ntiles > 1) lds_load_k(lk1, kbase + kTileBytes, ldr, w);
     wait_lds_loads_and_sync();
     v16i sa[2], sb[2];
     qk_tile(lk0, qa, hl, ql, sa);
@@ -249,8 +305,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
     // the previous step finished reading before its barrier.  Buffer parity is
     // t's: even steps fill lk0/lv0 and read lk1/lv1, odd steps the reverse.
     auto prefetch = [&](int tt, v4i *lkw, v4i *lvw) {
-        if (tt + 2 < ntiles) lds_load_k(lkw, kbase + (int64_t)(tt + 2) * kTileBytes, w, lane);
-        lds_load_v(lvw, vbase + (int64_t)tt * kTileBytes, w, lane);
+        if (tt + 2 < ntiles) lds_load_k(lkw, kbase + (int64_t)(tt + 2) * kTileBytes, ldr, w);
+        lds_load_v(lvw, vbase + (int64_t)tt * kTileBytes, ldr, w);
     };
 
     // step 0 (no P.V yet)
@@ -294,7 +350,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
         wait_lds_loads_and_sync();
     }
     // drain: P.V of the last tile (V(ntiles-1) sits in the buffer of its parity)
-    rescale(rs.alpha, o);
     if ((ntiles - 1) & 1) pv_tile(lv1, rs.pf, hl, ql, o);
     else pv_tile(lv0, rs.pf, hl, ql, o);
     const float lsum = rs.lsum;
