@@ -68,9 +68,9 @@ typedef enum {
 
 /* A [B, N, H, D] bf16 view: element (b, n, h, d) is at
  * data + b*stride_b + n*stride_n + h*stride_h + d (strides in elements).
- * data must be 16-byte aligned and stride_n, stride_h multiples of 8 (so every
- * 128-channel head row is 16-byte aligned); |stride_h| >= D and the views must
- * not alias across (n, h).  Strides may not be negative. */
+ * data must be 16-byte aligned and all strides multiples of 8 (so every
+ * 128-channel head row is 16-byte aligned); strides may not be negative.
+ * Input views are only read and may overlap (e.g. a broadcast head). */
 typedef struct {
     const void *data;
     int64_t stride_b, stride_n, stride_h;
@@ -80,6 +80,9 @@ typedef struct {
     void *data;
     int64_t stride_b, stride_n, stride_h;
 } sage_bf16_out;
+
+/* An output view: as above, 8-byte aligned, strides multiples of 4; the
+ * (b, n, h) rows of D elements must be disjoint (else SAGE_ERR_STRIDE). */
 
 /* round_up(N, SAGE_N_ALIGN); 0 for N < 1. */
 int64_t sage_npad(int N);
@@ -149,7 +152,8 @@ int sage_attn_fwd(const int8_t *q_codes, const float *q_scale, const int8_t *k_c
 
 /* The unquantised comparison path: the same softmax(Q K^T * sm_scale) V straight
  * from the strided bf16 views, BF16 MFMA for Q K^T and P.V (P rounded to bf16),
- * fp32 online softmax over 64-key tiles.  Output as sage_attn_fwd. */
+ * fp32 online softmax over 64-key tiles.  Output as sage_attn_fwd.  K and V
+ * token rows must not overlap: 128 <= stride_n <= 2^23 (else SAGE_ERR_STRIDE). */
 int sage_attn_fwd_bf16(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v,
                        int B, int N, int H, int D, float sm_scale, const sage_bf16_out *out,
                        void *stream);

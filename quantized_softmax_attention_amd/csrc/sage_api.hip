@@ -147,6 +147,10 @@ int sage_attn_fwd_bf16(const sage_bf16_in *q, const sage_bf16_in *k, const sage_
                        int D, float sm_scale, const sage_bf16_out *out, void *stream) {
     int st;
     if ((st = check_in(q)) || (st = check_in(k)) || (st = check_in(v))) return st;
+    // K and V tiles are staged as 64 token rows through 32-bit, row-bounded
+    // buffer offsets: token rows may not overlap and a tile must span < 2 GiB.
+    for (const sage_bf16_in *x : {k, v})
+        if (x->stride_n < kD || x->stride_n > (int64_t)1 << 23) return SAGE_ERR_STRIDE;
     if ((st = check_shape(B, N, H, D))) return st;
     if ((st = check_out(out, B, N, H))) return st;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_VALUE;

@@ -10,9 +10,13 @@
 //
 // Layout per wave mirrors the quantised kernel: K is the A operand and Q^T the
 // B operand, so each lane holds one query and 16 keys of every 32-key block;
-// those values are, unchanged, the P^T B operand of the second product once V
-// is staged transposed ([channel][key]) in LDS.  For k-step ks (16 keys) lane
-// half u element j pairs with key 16*ks + 8*(j/4) + 4*u + j%4.
+// those values are, unchanged, the P^T B operand of the second product.  For
+// k-step ks (16 keys) lane half u element e pairs with key
+// 16*ks + 8*(e/4) + 4*u + e%4.  K and V tiles are staged row-major ([key][128
+// channels], 256 B per row) straight from HBM into LDS; the V^T operand (one
+// channel, 4 keys per lane) comes from ds_read_b64_tr_b16, which within each
+// 16-lane group hands lane i element i%4 of the 8-byte reads of lanes
+// 4j + i/4, j = 0..3.
 #include "sage_common.h"
 
 namespace sage {
@@ -22,15 +26,24 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kQWg = 32 * kWaves;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = kD * 2;                 // 256 B per key row
+constexpr int kTileBytes16 = kTile * kRowBytes;   // 16 KB per K or V tile
+constexpr int kChunks16 = kTileBytes16 / 16;      // 1024 16-byte chunks
 constexpr float kLog2E = 1.4426950408889634f;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-// K tile [64 keys][128 ch] bf16 = 16 chunks of 16 B per row, XOR-swizzled.
-__device__ __forceinline__ int k_slot(int r, int c) { return r * 16 + (c ^ (r & 15)); }
-// V^T tile [128 ch][64 keys] bf16 = 16 units of 8 B per row, XOR-swizzled.
-__device__ __forceinline__ int v_unit(int d, int u) { return d * 16 + (u ^ ((d ^ (d >> 4)) & 15)); }
+// Stored 16-byte chunk of source chunk c (0..15) in key row r.  K: fragment
+// reads take one chunk of 16 consecutive rows per 16-lane cycle, so c ^ (r % 16)
+// spreads them over all 16 slots of a 256-byte bank line.  V: each 32-lane cycle
+// of a transposing read takes 8 bytes from 4 consecutive rows x 8 units, and
+// c ^ 4 (r % 4) puts the four rows on different 64-byte quarters.
+__device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int v_chunk(int r, int c) { return c ^ ((r & 3) << 2); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -48,115 +61,160 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-struct Prefetch {
-    uint4 k[4];   // K rows t/16 + 16*i, channels 8*(t%16)..+7
-    uint4 v[4];   // V keys 4*(t/16) + i, channels 8*(t%16)..+7
+// HBM -> LDS staging of a 64-row tile of a strided view (buffer_load ... lds).
+// Wave w issues LDS slots [256 w, 256 w + 256); lane L of instruction i writes
+// slot 256 w + 64 i + L.  The descriptor's record limit is the tile's valid
+// rows, so rows at or beyond N read as zero.
+struct Loader16 {
+    int koff[4], voff[4];   // per-lane source byte offsets within a K / V tile
 };
 
-__device__ __forceinline__ void load_tile(Prefetch &p, const View &K, const View &V, int64_t koff, int64_t voff,
-                                          int key0, int N, int t) {
-    const int row = t >> 4, seg = t & 15;
+__device__ __forceinline__ Loader16 make_loader16(int w, int lane, int64_t krow_bytes, int64_t vrow_bytes) {
+    Loader16 L;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        int nk = key0 + row + 16 * i;
-        int nv = key0 + 4 * row + i;
-        p.k[i] = nk < N ? *reinterpret_cast<const uint4 *>(K.data + koff + (int64_t)nk * K.sn + seg * 8)
-                        : make_uint4(0, 0, 0, 0);
-        p.v[i] = nv < N ? *reinterpret_cast<const uint4 *>(V.data + voff + (int64_t)nv * V.sn + seg * 8)
-                        : make_uint4(0, 0, 0, 0);
+        const int slot = 256 * w + 64 * i + lane;
+        const int r = slot >> 4, cs = slot & 15;
+        L.koff[i] = (int)(r * krow_bytes) + 16 * k_chunk(r, cs);   // k_chunk is an involution
+        L.voff[i] = (int)(r * vrow_bytes) + 16 * v_chunk(r, cs);
     }
+    return L;
 }
 
-__device__ __forceinline__ void store_tile(const Prefetch &p, uint4 *lk, uint2 *lv, int t) {
-    const int row = t >> 4, seg = t & 15;
+__device__ __forceinline__ void lds_load(v4i *lbuf, const uint16_t *tile, int rows_valid, int64_t row_bytes,
+                                         const int (&off)[4], int w) {
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(tile), 0,
+                                                      (int)(rows_valid * row_bytes), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; i++) lk[k_slot(row + 16 * i, seg)] = p.k[i];
-    // transpose 4 keys x 8 channels: channel c gets keys 4*row..4*row+3 (8 bytes)
-    uint32_t w[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        w[i][0] = p.v[i].x; w[i][1] = p.v[i].y; w[i][2] = p.v[i].z; w[i][3] = p.v[i].w;
-    }
-#pragma unroll
-    for (int c = 0; c < 8; c++) {
-        const int sh = (c & 1) ? 16 : 0;
-        uint32_t e0 = (w[0][c >> 1] >> sh) & 0xFFFFu, e1 = (w[1][c >> 1] >> sh) & 0xFFFFu;
-        uint32_t e2 = (w[2][c >> 1] >> sh) & 0xFFFFu, e3 = (w[3][c >> 1] >> sh) & 0xFFFFu;
-        lv[v_unit(seg * 8 + c, row)] = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-    }
+    for (int i = 0; i < 4; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(lbuf + 256 * w + 64 * i), 16, off[i], 0, 0, 0);
+}
+
+__device__ __forceinline__ void wait_lds_loads_and_sync() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// QK^T MFMA i (0..15): block i%2, 16-channel k-step i/2.
+__device__ __forceinline__ void qk_mfma(const v4i *lk, const v8bf (&qa)[8], int hl, int ql, v16f (&s)[2], int i) {
+    const int kb = i & 1, st = i >> 1;
+    const int r = 32 * kb + ql;
+    v8bf ka = __builtin_bit_cast(v8bf, lk[r * 16 + k_chunk(r, 2 * st + hl)]);
+    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[st], st ? s[kb] : v16f{}, 0, 0, 0);
+}
+
+// V^T operand of k-step ks, channel block db: two transposing reads (keys
+// 16ks + 4u + 0..3 and 16ks + 8 + 4u + 0..3).  Lane s = 4j + a of each 16-lane
+// group reads 4 channels (a quad) of key row 16ks + 4u + j.
+__device__ __forceinline__ v8bf v_operand(const v4i *lv, int lane, int ks, int db) {
+    const int g = lane >> 4, s = lane & 15, j = s >> 2, a = s & 3;
+    const int u = g >> 1, g2 = g & 1;
+    const int c = 4 * db + 2 * g2 + (a >> 1);                // source 16-byte chunk of the channel quad
+    const char *base = reinterpret_cast<const char *>(lv);
+    const int r0 = 16 * ks + 4 * u + j, r1 = r0 + 8;
+    lds_v4s *p0 = (lds_v4s *)(base + r0 * kRowBytes + 16 * v_chunk(r0, c) + 8 * (a & 1));
+    lds_v4s *p1 = (lds_v4s *)(base + r1 * kRowBytes + 16 * v_chunk(r1, c) + 8 * (a & 1));
+    v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+    v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+    typedef short v8s __attribute__((ext_vector_type(8)));
+    v8s both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(v8bf, both);
 }
 
 template <bool TAIL>
-__device__ __forceinline__ void tile_step(const uint4 *lk, const uint2 *lv, const v8bf (&qa)[8], float c2,
-                                          int nvalid, int hl, int ql, float &m2, float &lsum, v16f (&o)[4]) {
-    v16f s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-        s[kb] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int st = 0; st < 8; st++) {
-            v8bf ka = __builtin_bit_cast(v8bf, lk[k_slot(32 * kb + ql, 2 * st + hl)]);
-            s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qa[st], s[kb], 0, 0, 0);
-        }
-    }
+__device__ __forceinline__ float tile_max(v16f (&s)[2], float c2, int nvalid, int hl, float m2) {
     if (TAIL) {
 #pragma unroll
         for (int kb = 0; kb < 2; kb++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                int key = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-                if (key >= nvalid) s[kb][r] = -INFINITY;
-            }
+            for (int r = 0; r < 16; r++)
+                if (32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3) >= nvalid) s[kb][r] = -INFINITY;
     }
-    float smax = -INFINITY;
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
+    for (int r = 3; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[0][r]), s[0][r + 1]);
+    mx = fmaxf(fmaxf(mx, s[0][15]), s[1][0]);
 #pragma unroll
-        for (int r = 0; r < 16; r++) smax = fmaxf(smax, s[kb][r]);
-    smax = pair_max(smax);
-    const float mnew = fmaxf(m2, c2 * smax);
-    const float alpha = fast_exp2(m2 - mnew);
+    for (int r = 1; r < 15; r += 2) mx = fmaxf(fmaxf(mx, s[1][r]), s[1][r + 1]);
+    mx = fmaxf(mx, s[1][15]);
+    mx = pair_max(mx);
+    return fmaxf(m2, c2 * mx);
+}
+
+// p = exp(s - m) for registers 4c..4c+3 (c = 0..7), summed in fp32, packed to
+// bf16 pairs: registers r..r+3 of block kb are elements e0..e0+3 of k-step
+// 2 kb + r/8, e0 = r % 8.
+template <bool TAIL>
+__device__ __forceinline__ void tile_exp_chunk(const v16f (&s)[2], float c2, float mnew, int nvalid, int hl, int c,
+                                               uint32_t (&pw)[16], float &part) {
+    const int kb = c >> 2, r = 4 * (c & 3);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        p[i] = fast_exp2(c2 * s[kb][r + i] - mnew);
+        if (TAIL && 32 * kb + 8 * (r >> 2) + 4 * hl + i >= nvalid) p[i] = 0.0f;
+    }
+    part += (p[0] + p[1]) + (p[2] + p[3]);
+    const int ks = 2 * kb + (r >> 3), e0 = r & 7;
+    pw[4 * ks + (e0 >> 1)] = pack_bf16(p[0], p[1]);
+    pw[4 * ks + (e0 >> 1) + 1] = pack_bf16(p[2], p[3]);
+}
+
+__device__ __forceinline__ void pv_tile(const v4i *lv, const uint32_t (&pw)[16], int lane, v16f (&o)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+        const v8bf pb = __builtin_bit_cast(v8bf, make_uint4(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]));
+#pragma unroll
+        for (int db = 0; db < 4; db++)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(lv, lane, ks, db), pb, o[db], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void rescale(float alpha, v16f (&o)[4]) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-        lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; db++)
 #pragma unroll
             for (int r = 0; r < 16; r++) o[db][r] *= alpha;
     }
-    m2 = mnew;
+}
 
-    // P^T operand for k-step ks = 2*kb + half: registers 8*half .. 8*half+7 of block kb.
-    uint32_t pw[16];
+struct RowState {
+    float m2, lsum;
+    uint32_t pw[16];   // bf16 P^T operand of the last processed tile (its P.V pending)
+};
+
+// One pipeline step (see the quantised kernel): P.V of tile t-1, max and exp of
+// tile t with the 16 QK^T MFMAs of tile t+1 interleaved, then the rescale.
+template <bool PV, bool QK, bool TAIL>
+__device__ __forceinline__ void step(v16f (&s)[2], v16f (&sn)[2], const v4i *lk_next, const v4i *lv_prev,
+                                     const v8bf (&qa)[8], float c2, int nvalid, int lane, int hl, int ql,
+                                     RowState &st, v16f (&o)[4]) {
+    if (PV) pv_tile(lv_prev, st.pw, lane, o);
+    const float mnew = tile_max<TAIL>(s, c2, nvalid, hl, st.m2);
+    const float alpha = fast_exp2(st.m2 - mnew);
+    st.m2 = mnew;
     float part = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            float p0 = fast_exp2(c2 * s[kb][r] - mnew);
-            float p1 = fast_exp2(c2 * s[kb][r + 1] - mnew);
-            part += p0 + p1;
-            pw[(16 * kb + r) >> 1] = pack_bf16(p0, p1);
+    for (int c = 0; c < 8; c++) {
+        if (QK) {
+            qk_mfma(lk_next, qa, hl, ql, sn, 2 * c);
+            qk_mfma(lk_next, qa, hl, ql, sn, 2 * c + 1);
         }
-    lsum += part;
-
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-        v8bf pb = __builtin_bit_cast(v8bf, make_uint4(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]));
-#pragma unroll
-        for (int db = 0; db < 4; db++) {
-            const int d = 32 * db + ql;
-            uint2 lo = lv[v_unit(d, 4 * ks + hl)];       // keys 16ks + 4hl + 0..3
-            uint2 hi = lv[v_unit(d, 4 * ks + 2 + hl)];   // keys 16ks + 8 + 4hl + 0..3
-            v8bf va = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[db], 0, 0, 0);
-        }
+        tile_exp_chunk<TAIL>(s, c2, mnew, nvalid, hl, c, st.pw, part);
     }
+    asm volatile("" ::"v"(st.pw[0]), "v"(st.pw[4]), "v"(st.pw[8]), "v"(st.pw[12]), "v"(part));
+    if (QK) asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    st.lsum = st.lsum * alpha + part;
+    if (PV) rescale(alpha, o);
 }
 
 __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(View Q, View K, View V, int N, int H, float c2,
                                                                OutView out, int nqwg) {
-    __shared__ uint4 lk[2][64 * 16];
-    __shared__ uint2 lv[2][128 * 16];
+    __shared__ v4i lk0[kChunks16], lk1[kChunks16], lv0[kChunks16], lv1[kChunks16];
 
     const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
     const int qb = (int)(id % (uint32_t)nqwg);
@@ -174,33 +232,76 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(View Q, View K, 
             qa[st] = __builtin_bit_cast(
                 v8bf, n < N ? *reinterpret_cast<const uint4 *>(qrow + 16 * st) : make_uint4(0, 0, 0, 0));
     }
-    const int64_t koff = (int64_t)b * K.sb + (int64_t)h * K.sh;
-    const int64_t voff = (int64_t)b * V.sb + (int64_t)h * V.sh;
+    const uint16_t *kbase = K.data + (int64_t)b * K.sb + (int64_t)h * K.sh;
+    const uint16_t *vbase = V.data + (int64_t)b * V.sb + (int64_t)h * V.sh;
+    const int64_t krow = K.sn * 2, vrow = V.sn * 2;
+    const Loader16 ldr = make_loader16(w, lane, krow, vrow);
     const int ntiles = (N + kTile - 1) / kTile;
     const int tail_valid = N - (ntiles - 1) * kTile;
+    const bool partial = tail_valid != kTile;
+    auto rows = [&](int tt) { return min(kTile, N - tt * kTile); };
 
     v16f o[4];
 #pragma unroll
     for (int db = 0; db < 4; db++) o[db] = v16f{0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    float m2 = -INFINITY, lsum = 0.0f;
+    RowState rs;
+    rs.m2 = -INFINITY;
+    rs.lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) rs.pw[i] = 0;
 
-    Prefetch pre;
-    load_tile(pre, K, V, koff, voff, 0, N, t);
-    store_tile(pre, lk[0], lv[0], t);
+    lds_load(lk0, kbase, rows(0), krow, ldr.koff, w);
+    if (ntiles > 1) lds_load(lk1, kbase + (int64_t)kTile * K.sn, rows(1), krow, ldr.koff, w);
+    wait_lds_loads_and_sync();
+    v16f sa[2], sb[2];
+#pragma unroll
+    for (int i = 0; i < 16; i++) qk_mfma(lk0, qa, hl, ql, sa, i);
     __syncthreads();
-    for (int tt = 0; tt < ntiles; tt++) {
-        const int buf = tt & 1;
-        const bool more = tt + 1 < ntiles;
-        if (more) load_tile(pre, K, V, koff, voff, (tt + 1) * kTile, N, t);
-        if (more || tail_valid == kTile)
-            tile_step<false>(lk[buf], lv[buf], qa, c2, kTile, hl, ql, m2, lsum, o);
-        else
-            tile_step<true>(lk[buf], lv[buf], qa, c2, tail_valid, hl, ql, m2, lsum, o);
-        if (more) store_tile(pre, lk[buf ^ 1], lv[buf ^ 1], t);
-        __syncthreads();
-    }
 
-    const float inv = 1.0f / pair_sum(lsum);
+    auto prefetch = [&](int tt, v4i *lkw, v4i *lvw) {
+        if (tt + 2 < ntiles) lds_load(lkw, kbase + (int64_t)(tt + 2) * kTile * K.sn, rows(tt + 2), krow, ldr.koff, w);
+        lds_load(lvw, vbase + (int64_t)tt * kTile * V.sn, rows(tt), vrow, ldr.voff, w);
+    };
+
+    prefetch(0, lk0, lv0);
+    if (ntiles == 1) {
+        if (partial) step<false, false, true>(sa, sb, lk1, lv1, qa, c2, tail_valid, lane, hl, ql, rs, o);
+        else step<false, false, false>(sa, sb, lk1, lv1, qa, c2, kTile, lane, hl, ql, rs, o);
+    } else {
+        step<false, true, false>(sa, sb, lk1, lv1, qa, c2, kTile, lane, hl, ql, rs, o);
+    }
+    wait_lds_loads_and_sync();
+    int tt = 1;
+    for (; tt + 2 < ntiles; tt += 2) {
+        prefetch(tt, lk1, lv1);
+        step<true, true, false>(sb, sa, lk0, lv0, qa, c2, kTile, lane, hl, ql, rs, o);
+        wait_lds_loads_and_sync();
+        prefetch(tt + 1, lk0, lv0);
+        step<true, true, false>(sa, sb, lk1, lv1, qa, c2, kTile, lane, hl, ql, rs, o);
+        wait_lds_loads_and_sync();
+    }
+    if (tt + 1 < ntiles) {
+        prefetch(tt, lk1, lv1);
+        step<true, true, false>(sb, sa, lk0, lv0, qa, c2, kTile, lane, hl, ql, rs, o);
+        wait_lds_loads_and_sync();
+        tt++;
+    }
+    if (tt < ntiles) {
+        if (tt & 1) {
+            prefetch(tt, lk1, lv1);
+            if (partial) step<true, false, true>(sb, sa, lk0, lv0, qa, c2, tail_valid, lane, hl, ql, rs, o);
+            else step<true, false, false>(sb, sa, lk0, lv0, qa, c2, kTile, lane, hl, ql, rs, o);
+        } else {
+            prefetch(tt, lk0, lv0);
+            if (partial) step<true, false, true>(sa, sb, lk1, lv1, qa, c2, tail_valid, lane, hl, ql, rs, o);
+            else step<true, false, false>(sa, sb, lk1, lv1, qa, c2, kTile, lane, hl, ql, rs, o);
+        }
+        wait_lds_loads_and_sync();
+    }
+    if ((ntiles - 1) & 1) pv_tile(lv1, rs.pw, lane, o);
+    else pv_tile(lv0, rs.pw, lane, o);
+
+    const float inv = 1.0f / pair_sum(rs.lsum);
     if (n < N) {
         uint16_t *orow = out.data + (int64_t)b * out.sb + (int64_t)n * out.sn + (int64_t)h * out.sh;
 #pragma unroll

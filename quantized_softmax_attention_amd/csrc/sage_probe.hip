@@ -60,6 +60,17 @@ __global__ void probe_swap_kernel(const int *x, int *out) {
     out[64 + l] = r[1];
 }
 
+// in: 4096 bf16/i16 values staged in LDS; addr: per-lane byte addresses (each
+// < 8192 - 8, 8-byte aligned); out: [64 lanes][4] results of ds_read_b64_tr_b16.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__global__ void probe_tr16_kernel(const short *in, const int *addr, v4s *out) {
+    __shared__ short lds[4096];
+    for (int i = threadIdx.x; i < 4096; i += 64) lds[i] = in[i];
+    __syncthreads();
+    int a = addr[threadIdx.x];
+    out[threadIdx.x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(lds + a / 2));
+}
+
 __global__ void probe_exp2_kernel(const float *x, int n, float *out) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) out[i] = __builtin_amdgcn_exp2f(x[i]);
@@ -102,6 +113,12 @@ int sage_probe_cvt_fp8(const float *x, int n, uint8_t *out) {
 
 int sage_probe_swap(const int *x, int *out) {
     hipLaunchKernelGGL(probe_swap_kernel, dim3(1), dim3(64), 0, 0, x, out);
+    hipError_t e = hipGetLastError();
+    return e != hipSuccess ? (int)e : (int)hipDeviceSynchronize();
+}
+
+int sage_probe_tr16(const short *in, const int *addr, short *out) {
+    hipLaunchKernelGGL(probe_tr16_kernel, dim3(1), dim3(64), 0, 0, in, addr, (v4s *)out);
     hipError_t e = hipGetLastError();
     return e != hipSuccess ? (int)e : (int)hipDeviceSynchronize();
 }

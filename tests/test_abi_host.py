@@ -119,3 +119,8 @@ def test_attn_fwd_bf16_validation():
     assert call(view(data=A + 2)) == ALIGN
     assert call(view(), o=out(sh=0)) == STRIDE
     assert call(view(), sm=float("inf")) == VALUE
+    # K/V token rows must not overlap on this path
+    L2 = sage.lib()
+    k_bad = sage.BF16In(A, N * 3 * H * D, 64, D)
+    assert L2.sage_attn_fwd_bf16(ctypes.byref(view()), ctypes.byref(k_bad), ctypes.byref(view()), B, N, H, D, 0.1,
+                                 ctypes.byref(out()), None) == STRIDE

@@ -172,3 +172,22 @@ def test_exp2_accuracy(probe):
     fin = np.isfinite(x)
     rel = np.abs(got[fin] - want[fin]) / want[fin]
     assert rel.max() <= 4 * 2.0 ** -23, rel.max()
+
+
+def test_ds_read_tr16_b64_lane_rule(probe):
+    # Within each 16-lane group the 16 lanes' 8-byte reads form a 16x4 matrix
+    # M[s][c] (s = lane in group, c = element); output lane i holds
+    # M[4j + i//4][i % 4] for j = 0..3.
+    vals = torch.arange(4096, dtype=torch.int16, device="cuda")
+    rng = np.random.default_rng(7)
+    addr = (rng.integers(0, 4096 // 4 - 1, 64) * 8).astype(np.int32)    # random 8-byte aligned rows
+    ta = torch.from_numpy(addr).cuda()
+    out = torch.zeros(64 * 4, dtype=torch.int16, device="cuda")
+    assert probe.sage_probe_tr16(ctypes.c_void_p(vals.data_ptr()), ctypes.c_void_p(ta.data_ptr()),
+                                 ctypes.c_void_p(out.data_ptr())) == 0
+    got = out.cpu().numpy().reshape(64, 4)
+    src = (addr // 2)[:, None] + np.arange(4)[None, :]        # element indices each lane reads
+    for lane in range(64):
+        g, i = lane // 16, lane % 16
+        want = [src[16 * g + 4 * j + i // 4, i % 4] for j in range(4)]
+        assert list(got[lane]) == want, lane
