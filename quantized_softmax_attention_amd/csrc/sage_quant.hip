@@ -16,37 +16,33 @@
 namespace sage {
 
 // ------------------------------------------------------------------ K mean
-// Partial sums: one workgroup per (64-token chunk c, head h, batch b).  The
-// chunk is staged in LDS as fp32 (bf16 widens exactly) and thread d adds its
-// channel's 64 values in ascending token order in fp64.
+// Partial sums: thread (chunk c, channel group seg) adds its 8 channels over the
+// chunk's 64 tokens in ascending order in fp64 (bf16 widens exactly).  A
+// workgroup covers 16 chunks of one head; the 16 threads of a chunk read whole
+// 256-byte head rows.
 __global__ __launch_bounds__(256) void kmean_partial_kernel(View k, int N, int H, int nchunk,
                                                             double *__restrict__ ws) {
-    __shared__ float tile[kSumChunk][kD + 4];
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int c = blockIdx.x * 16 + (threadIdx.x >> 4), seg = threadIdx.x & 15;
+    if (c >= nchunk) return;
     const uint16_t *base = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
+    const int n0 = c * kSumChunk, n1 = min(N, n0 + kSumChunk);
+    double s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 8
+    for (int n = n0; n < n1; n++) {
+        const uint4 raw = *reinterpret_cast<const uint4 *>(base + (int64_t)n * k.sn);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-    for (int i = 0; i < kSumChunk / 16; i++) {
-        int r = row + 16 * i, n = c * kSumChunk + r;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (n < N) raw = *reinterpret_cast<const uint4 *>(base + (int64_t)n * k.sn);
-        uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int j = 0; j < 8; j++)
+            s[j] += (double)bf16_to_f32((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+    }
+    double *dst = ws + (((int64_t)b * nchunk + c) * H + h) * kD + seg * 8;
 #pragma unroll
-        for (int j = 0; j < 4; j++) {
-            tile[r][seg * 8 + 2 * j] = bf16_to_f32(w[j] & 0xFFFFu);
-            tile[r][seg * 8 + 2 * j + 1] = bf16_to_f32(w[j] >> 16);
-        }
-    }
-    __syncthreads();
-    if (t < kD) {
-        int rows = min(kSumChunk, N - c * kSumChunk);
-        double s = 0.0;
-        for (int r = 0; r < rows; r++) s += (double)tile[r][t];
-        ws[(((int64_t)b * nchunk + c) * H + h) * kD + t] = s;
-    }
+    for (int j = 0; j < 8; j++) dst[j] = s[j];
 }
 
 // Total over chunks in ascending order, one fp64 division by N, one rounding.
+// The adds are a dependent chain, so loads are issued 32 at a time ahead of it.
 __global__ __launch_bounds__(256) void kmean_final_kernel(const double *__restrict__ ws, int N, int H,
                                                           int nchunk, int B, float *__restrict__ km) {
     int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -55,7 +51,15 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(const double *__restri
     int64_t b = i / HD, hd = i % HD;
     const double *p = ws + b * nchunk * HD + hd;
     double s = 0.0;
-    for (int c = 0; c < nchunk; c++) s += p[(int64_t)c * HD];
+    int c = 0;
+    for (; c + 32 <= nchunk; c += 32) {
+        double v[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) v[j] = p[(int64_t)(c + j) * HD];
+#pragma unroll
+        for (int j = 0; j < 32; j++) s += v[j];
+    }
+    for (; c < nchunk; c++) s += p[(int64_t)c * HD];
     km[i] = (float)(s / (double)N);
 }
 
@@ -192,7 +196,15 @@ __global__ __launch_bounds__(256) void v_amax_final_kernel(const float *__restri
     int64_t b = i / HD, hd = i % HD;
     const float *p = ws + b * nchunk * HD + hd;
     float a = 0.0f;
-    for (int c = 0; c < nchunk; c++) a = fmaxf(a, p[(int64_t)c * HD]);
+    int c = 0;
+    for (; c + 32 <= nchunk; c += 32) {   // loads issued 32 at a time (max is exact in any order)
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) v[j] = p[(int64_t)(c + j) * HD];
+#pragma unroll
+        for (int j = 0; j < 32; j++) a = fmaxf(a, v[j]);
+    }
+    for (; c < nchunk; c++) a = fmaxf(a, p[(int64_t)c * HD]);
     amax[i] = a;
     vs[i] = a / 448.0f;
 }
@@ -244,7 +256,8 @@ hipError_t launch_quantize_qk(View q, View k, int B, int N, int H, int8_t *qc, f
     const int nchunk = (N + kSumChunk - 1) / kSumChunk;
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     double *ws = static_cast<double *>(workspace);
-    hipLaunchKernelGGL(kmean_partial_kernel, dim3(nchunk, H, B), dim3(256), 0, stream, k, N, H, nchunk, ws);
+    hipLaunchKernelGGL(kmean_partial_kernel, dim3((nchunk + 15) / 16, H, B), dim3(256), 0, stream, k, N, H, nchunk,
+                       ws);
     int64_t total = (int64_t)B * H * kD;
     hipLaunchKernelGGL(kmean_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws, N,
                        H, nchunk, B, km);
