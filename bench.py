@@ -80,9 +80,10 @@ def load_traffic(kernel_src: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(case, rows_per_head=256, heads=4):
+def cpu_baseline(case, rows_per_head=512, heads=None):
     """Time the oracle: quantisers at full size, then the step-by-step
-    quantised attention on `rows_per_head` sampled rows of `heads` heads,
+    quantised attention on `rows_per_head` sampled rows (the last 64 plus
+    seeded random rows) of `heads` heads (all by default) against all keys,
     extrapolated to the whole call."""
     import numpy as np
 
@@ -97,6 +98,7 @@ def cpu_baseline(case, rows_per_head=256, heads=4):
     kc, ks = oracle.quant_k(k, km, 64)
     vc, vs = oracle.quant_v(v)
     t_quant = time.perf_counter() - t0
+    heads = case.H if heads is None else heads
     rows = inputs.sample_rows(case.B, case.H, case.N, count=rows_per_head, tail=64)[:, :heads]
     sub = lambda a: np.ascontiguousarray(a[:, :heads])
     t0 = time.perf_counter()
