@@ -194,6 +194,19 @@ __device__ __forceinline__ void rescale(float alpha, v16f (&o)[4]) {
     }
 }
 
+// MFMA operands read from LDS: K fragment i (block i%2, k-step i/2) of a tile and
+// the V fragment of channel block db.
+__device__ __forceinline__ v4i k_operand(const v4i *lk, int i, int hl, int ql) {
+    const int kb = i & 1, st = i >> 1;
+    return lk[k_slot(32 * kb + ql, 2 * st + hl)];
+}
+__device__ __forceinline__ v8i v_operand(const v4i *lv, int db, int hl, int ql) {
+    const int d = 32 * db + ql;
+    v4i lo = lv[v_slot(d, 2 * hl)];
+    v4i hi = lv[v_slot(d, 2 * hl + 1)];
+    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
 // Per-wave running state of the online softmax.
 struct RowState {
     float m2;     // running maximum, log2 units
@@ -212,7 +225,24 @@ template <bool PV, bool QK, bool TAIL>
 __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_next, const v4i *lv_prev,
                                      const v4i (&qa)[4], float c2, int nvalid, int hl, int ql, RowState &st,
                                      v16f (&o)[4]) {
-    if (PV) pv_tile(lv_prev, st.pf, hl, ql, o);   // O = alpha(t-1) acc(t-2) + P(t-1) V(t-1)
+    // MFMA operands are read from LDS ahead of their MFMA (V one MFMA ahead, K
+    // two), so an MFMA rarely waits for its LDS read and the VALU work behind
+    // it in issue order is not held up.
+    v8i va[2];
+    v4i ka[3];
+    if (PV) va[0] = v_operand(lv_prev, 0, hl, ql);
+    else if (QK) {
+        ka[0] = k_operand(lk_next, 0, hl, ql);
+        ka[1] = k_operand(lk_next, 1, hl, ql);
+    }
+    if (PV) {   // O = alpha(t-1) acc(t-2) + P(t-1) V(t-1)
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+            if (db < 3) va[(db + 1) & 1] = v_operand(lv_prev, db + 1, hl, ql);
+            if (QK && db >= 2) ka[db - 2] = k_operand(lk_next, db - 2, hl, ql);
+            o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db & 1], st.pf, o[db], 0, 0, 0, 127, 0, 127);
+        }
+    }
     const float mnew = tile_max<TAIL>(s, c2, nvalid, hl, st.m2);
     const float alpha = fast_exp2(st.m2 - mnew);   // 0 on the first tile (m2 = -inf)
     st.m2 = mnew;
@@ -220,24 +250,33 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
     float part = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; c++) {
-        if (QK) qk_mfma(lk_next, qa, hl, ql, sn, c);
+        if (QK) {
+            if (c < 6) ka[(c + 2) % 3] = k_operand(lk_next, c + 2, hl, ql);
+            const int kb = c & 1, kst = c >> 1;   // the two accumulation chains alternate
+            sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[c % 3], qa[kst], kst ? sn[kb] : v16i{}, 0, 0, 0);
+        }
         tile_exp_chunk<TAIL>(s, c2, bias, nvalid, hl, c, st.pf, part);
     }
     // Issue order for the region: the P.V MFMAs spread over the max reduction,
-    // then one QK^T MFMA (with its LDS read) per exp chunk.
+    // then one QK^T MFMA per exp chunk, each LDS read placed before the MFMA
+    // that precedes its own.
     if (PV) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);           // V operand 0
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // 2 LDS reads (V operand)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            if (i < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // V operand i+1
+            if (QK && i >= 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K operands 0, 1
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // P.V MFMA i
             __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // 6 VALU
         }
+    } else if (QK) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);       // K operands 0, 1
     }
     if (QK) {
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read (K operand)
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+            if (i < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // K operand i+2
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // QK^T MFMA i
             __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);  // 16 VALU
         }
     }
