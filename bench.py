@@ -12,6 +12,7 @@ Prints ONE JSON line.  Besides the contract keys it carries:
                    its duration is measured with HIP events on its own stream.
   stages        -- per-stage ms and the quantisers' achieved HBM bandwidth.
   bf16_path     -- the unquantised BF16-MFMA path on the same inputs.
+  int8qk_path   -- INT8 Q K^T with the bf16 V unquantised (BF16 P.V) on the same inputs.
   cpu_baseline  -- the CPU oracle (quantisers in full + step-by-step quantised
                    attention on sampled rows, extrapolated), on the host cores.
 
@@ -35,6 +36,7 @@ METRIC = "attention TFLOPS (4·N²·d·H/t) + ms/call at N=37810,H=56,d=128; % M
 PEAK_I8F8_TFLOPS = 5000.0      # MI355X dense INT8 (POP/s) and FP8 (FLOP/s)
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_INT8QK_TFLOPS = 1.0 / (0.5 / PEAK_I8F8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # INT8 QK^T + BF16 P.V
 B, N, H, D = 1, 37810, 56, 128
 
 
@@ -131,7 +133,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--bf16-calls", type=int, default=5)
+    ap.add_argument("--bf16-calls", type=int, default=5,
+                    help="timed calls of each comparison path (bf16, INT8-QK/bf16-PV)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one plain 1 GiB device copy (for HBM counter scaling)")
@@ -218,6 +221,16 @@ def main():
     stream.synchronize()
     bf16_ms = [e[0].elapsed_time(e[1]) for e in e16]
 
+    # INT8 Q K^T with the bf16 V unquantised (codes of the last step's quantise_qk)
+    eq = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.bf16_calls)]
+    sage.sage_attn_fwd_int8qk(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, g.v, out16, sm, stream)
+    for e in eq:
+        e[0].record(stream)
+        sage.sage_attn_fwd_int8qk(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, g.v, out16, sm, stream)
+        e[1].record(stream)
+    stream.synchronize()
+    int8qk_ms = [e[0].elapsed_time(e[1]) for e in eq]
+
     line = {
         "metric": METRIC,
         "value": value,
@@ -250,6 +263,10 @@ def main():
         "bf16_path": {"ms_per_call": stats_ms(bf16_ms),
                       "tflops": flops / (statistics.fmean(bf16_ms) * 1e-3) / 1e12,
                       "frac_of_bf16_peak": flops / (statistics.fmean(bf16_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "int8qk_path": {"ms_per_call": stats_ms(int8qk_ms),
+                        "tflops": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12,
+                        "frac_of_peak": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12 / PEAK_INT8QK_TFLOPS,
+                        "peak_note": "half the ops at the INT8 peak, half at the BF16 peak: 1/(0.5/5000 + 0.5/2500)"},
         "pages_context": {"gb10_attention_forward_p50_ms": 238.995, "gb10_total_excluding_layout_ms": 258.613,
                           "note": "NVIDIA GB10 on real activations; context only"},
         "input_generation_s": gen_s,

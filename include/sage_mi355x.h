@@ -158,6 +158,23 @@ int sage_attn_fwd_bf16(const sage_bf16_in *q, const sage_bf16_in *k, const sage_
                        int B, int N, int H, int D, float sm_scale, const sage_bf16_out *out,
                        void *stream);
 
+/* INT8 Q K^T with an unquantised P.V: the precision split the profile page runs
+ * as "sol_int8_qk" (sampling_stage_step_2_seconds.sol_int8_qk_tau_1_3_exact_
+ * conditioning_kv: Q and K quantised, V not), here dense and non-causal.  Scores
+ * come from the codes and scales sage_quantize_qk wrote, exactly as in
+ * sage_attn_fwd; then for every query i < N of every (b, h):
+ *   for 64-key tiles in ascending order (the last one partial, keys >= N absent):
+ *     m  <- max(m, max_j s_ij);  rescale l and acc by exp(m_old - m)
+ *     p_ij = exp(s_ij - m);  l += p_ij (fp32)
+ *     acc_d += bf16_rne(p_ij) * v[b, j, h, d]   (BF16 MFMA, fp32 accumulate)
+ *   out[b, i, h, d] = bf16_rne(acc_d / l).
+ * v is the bf16 [B, N, H, D] view (as for sage_attn_fwd_bf16: 16-byte aligned,
+ * strides multiples of 8, 128 <= stride_n <= 2^23 so token rows do not overlap).
+ * No V quantisation pass is needed.  Output and errors as sage_attn_fwd. */
+int sage_attn_fwd_int8qk(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes,
+                         const float *k_scale, const sage_bf16_in *v, int B, int N, int H, int D,
+                         float sm_scale, const sage_bf16_out *out, void *stream);
+
 /* A static, human-readable name for a sage_status value. */
 const char *sage_status_str(int status);
 

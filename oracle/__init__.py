@@ -67,8 +67,11 @@ def _load():
         lib.sage_oracle_attn_exact.argtypes = ([_p, _i64, _i64, _i64] * 3 +
                                                [_int, _int, _int, _int, _dbl, _p, _int, _p])
         lib.sage_oracle_attn_method.argtypes = ([_p] * 6 + [_int] * 7 + [_dbl, _dbl, _int, _p, _int, _p])
+        lib.sage_oracle_attn_int8qk.argtypes = ([_p] * 4 + [_p, _i64, _i64, _i64] + [_int] * 7 +
+                                                [_dbl, _int, _p, _int, _p])
         for f in ("sage_oracle_kmean", "sage_oracle_quant_q", "sage_oracle_quant_k", "sage_oracle_quant_v",
                   "sage_oracle_softmax_row", "sage_oracle_attn_exact", "sage_oracle_attn_method",
+                  "sage_oracle_attn_int8qk",
                   "sage_oracle_e4m3_encode_array", "sage_oracle_e4m3_decode_array"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -215,6 +218,24 @@ def attn_method(qc, qs, kc, ks, vc, vs, sm_scale: float, rows=None, qblk: int = 
     out = np.empty((B, H, R, D), dtype=np.float64)
     _load().sage_oracle_attn_method(pqc, pqs, pkc, pks, pvc, pvs, B, N, H, D, qblk, kblk, ptile,
                                     sm_scale, pscale, int(round_p), rows.ctypes.data, R, out.ctypes.data)
+    return out
+
+
+def attn_int8qk(qc, qs, kc, ks, v: View, sm_scale: float, rows=None, qblk: int = 32, kblk: int = 64,
+                ptile: int = 64, round_p: bool = True) -> np.ndarray:
+    """INT8 Q K^T from logical codes/scales with the bf16 V view unquantised and
+    P rounded to bf16 for the product; returns [B, H, R, D]."""
+    B, H, N, D = qc.shape
+    qc, pqc = _c(qc, np.int8)
+    kc, pkc = _c(kc, np.int8)
+    qs, pqs = _c(qs, np.float32)
+    ks, pks = _c(ks, np.float32)
+    assert kc.shape == (B, H, N, D) and (v.B, v.N, v.H, v.D) == (B, N, H, D)
+    assert qs.shape == (B, H, -(-N // qblk)) and ks.shape == (B, H, -(-N // kblk))
+    rows, R = _rows(all_rows(B, H, N) if rows is None else rows, B, H)
+    out = np.empty((B, H, R, D), dtype=np.float64)
+    _load().sage_oracle_attn_int8qk(pqc, pqs, pkc, pks, *v.args(), B, N, H, D, qblk, kblk, ptile, sm_scale,
+                                    int(round_p), rows.ctypes.data, R, out.ctypes.data)
     return out
 
 

@@ -380,6 +380,89 @@ void sage_oracle_attn_method(const int8_t *qc, const float *qs, const int8_t *kc
     }
 }
 
+/* ------------------------------ INT8 Q K^T with an unquantised P.V ---- */
+/* bf16 of an fp32 value: round to nearest, ties to even (finite values), as the
+ * bfloat16 format is defined (the upper 16 bits of an IEEE binary32). */
+static double bf16_rne(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1u;
+    u = upper << 16;
+    float r;
+    memcpy(&r, &u, sizeof r);
+    return (double)r;
+}
+
+/* The "sol_int8_qk" precision split of the profile page
+ * (sampling_stage_step_2_seconds.sol_int8_qk_tau_1_3_exact_conditioning_kv:
+ * Q and K quantised, V not), dense.  Scores and the tile walk are those of
+ * sage_oracle_attn_method; V is the bf16 view itself:
+ *   for key tiles of `ptile` keys in ascending order:
+ *     m_t = max(m_{t-1}, max_j s_ij);  alpha = exp(m_{t-1} - m_t)
+ *     p_ij = exp(s_ij - m_t);  l = alpha * l + sum_j p_ij        unrounded p
+ *     acc_d = alpha * acc_d + sum_j bf16(fp32(p_ij)) * v_jd      (if round_p)
+ *   o_id = acc_d / l
+ * Reading: P is rounded to bf16 from its fp32 value (the precision the kernel
+ * holds p in) relative to the running maximum after each tile, as for E4M3 P in
+ * the fully quantised method. */
+void sage_oracle_attn_int8qk(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks,
+                             const uint16_t *v, i64 vsb, i64 vsn, i64 vsh,
+                             int B, int N, int H, int D, int qblk, int kblk, int ptile,
+                             double sm_scale, int round_p, const int *rows, int nrows, double *out)
+{
+    int nqb = (N + qblk - 1) / qblk, nkb = (N + kblk - 1) / kblk;
+#pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)ptile);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp for collapse(3) schedule(dynamic, 4)
+        for (int b = 0; b < B; b++)
+            for (int h = 0; h < H; h++)
+                for (int r = 0; r < nrows; r++) {
+                    i64 bh = (i64)b * H + h;
+                    int i = rows[bh * nrows + r];
+                    const int8_t *qi = qc + (bh * N + i) * D;
+                    double sq = qs[bh * nqb + i / qblk];
+                    double m = -INFINITY, l = 0.0;
+                    for (int d = 0; d < D; d++)
+                        acc[d] = 0.0;
+                    for (int j0 = 0; j0 < N; j0 += ptile) {
+                        int j1 = j0 + ptile < N ? j0 + ptile : N;
+                        double mt = m;
+                        for (int j = j0; j < j1; j++) {
+                            const int8_t *kj = kc + (bh * N + j) * D;
+                            i64 a = 0;
+                            for (int d = 0; d < D; d++)
+                                a += (i64)qi[d] * (i64)kj[d];
+                            s[j - j0] = (double)a * sq * (double)ks[bh * nkb + j / kblk] * sm_scale;
+                            if (s[j - j0] > mt)
+                                mt = s[j - j0];
+                        }
+                        double alpha = exp(m - mt); /* m = -inf on the first tile: 0 */
+                        l *= alpha;
+                        for (int d = 0; d < D; d++)
+                            acc[d] *= alpha;
+                        for (int j = j0; j < j1; j++) {
+                            double p = exp(s[j - j0] - mt);
+                            double pq = round_p ? bf16_rne((float)p) : p;
+                            l += p;
+                            for (int d = 0; d < D; d++)
+                                acc[d] += pq * (double)load_bf16(v, vsb, vsn, vsh, b, j, h, d);
+                        }
+                        m = mt;
+                    }
+                    double *o = out + (bh * nrows + r) * D;
+                    for (int d = 0; d < D; d++)
+                        o[d] = acc[d] / l;
+                }
+        free(s);
+        free(acc);
+    }
+}
+
 /* Threads the OpenMP loops above use (reported beside oracle timings). */
 #ifdef _OPENMP
 #include <omp.h>

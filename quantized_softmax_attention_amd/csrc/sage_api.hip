@@ -15,6 +15,8 @@ hipError_t launch_attn_fwd(const int8_t *qc, const float *qs, const int8_t *kc, 
                            const float *vs, int B, int N, int H, float sm_scale, OutView out, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(View q, View k, View v, int B, int N, int H, float sm_scale, OutView out,
                                 hipStream_t stream);
+hipError_t launch_attn_fwd_int8qk(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, View v,
+                                  int B, int N, int H, float sm_scale, OutView out, hipStream_t stream);
 }  // namespace sage
 
 namespace {
@@ -80,6 +82,13 @@ sage::OutView to_out(const sage_bf16_out *o) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
+
+// K and V tiles of a strided view are staged as 64 token rows through 32-bit,
+// row-bounded buffer offsets: token rows may not overlap and a tile must span
+// < 2 GiB.
+int check_tile_rows(const sage_bf16_in *x) {
+    return (x->stride_n < kD || x->stride_n > (int64_t)1 << 23) ? SAGE_ERR_STRIDE : SAGE_OK;
+}
 
 }  // namespace
 
@@ -147,15 +156,28 @@ int sage_attn_fwd_bf16(const sage_bf16_in *q, const sage_bf16_in *k, const sage_
                        int D, float sm_scale, const sage_bf16_out *out, void *stream) {
     int st;
     if ((st = check_in(q)) || (st = check_in(k)) || (st = check_in(v))) return st;
-    // K and V tiles are staged as 64 token rows through 32-bit, row-bounded
-    // buffer offsets: token rows may not overlap and a tile must span < 2 GiB.
-    for (const sage_bf16_in *x : {k, v})
-        if (x->stride_n < kD || x->stride_n > (int64_t)1 << 23) return SAGE_ERR_STRIDE;
+    if ((st = check_tile_rows(k)) || (st = check_tile_rows(v))) return st;
     if ((st = check_shape(B, N, H, D))) return st;
     if ((st = check_out(out, B, N, H))) return st;
     if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_VALUE;
     return hip_status(sage::launch_attn_fwd_bf16(to_view(q), to_view(k), to_view(v), B, N, H, sm_scale, to_out(out),
                                                  static_cast<hipStream_t>(stream)));
+}
+
+int sage_attn_fwd_int8qk(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes, const float *k_scale,
+                         const sage_bf16_in *v, int B, int N, int H, int D, float sm_scale, const sage_bf16_out *out,
+                         void *stream) {
+    int st;
+    if (!q_codes || !q_scale || !k_codes || !k_scale) return SAGE_ERR_NULL;
+    if ((st = check_in(v))) return st;
+    if ((st = check_tile_rows(v))) return st;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if ((st = check_out(out, B, N, H))) return st;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(q_scale, 4) || !aligned(k_scale, 4))
+        return SAGE_ERR_ALIGN;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_VALUE;
+    return hip_status(sage::launch_attn_fwd_int8qk(q_codes, q_scale, k_codes, k_scale, to_view(v), B, N, H, sm_scale,
+                                                   to_out(out), static_cast<hipStream_t>(stream)));
 }
 
 const char *sage_status_str(int status) {

@@ -65,7 +65,8 @@ def lib() -> ctypes.CDLL:
         L.sage_quantize_v.argtypes = [pin, i, i, i, i, vp, vp, vp, sz, vp]
         L.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_bf16.argtypes = [pin, pin, pin, i, i, i, i, f, pout, vp]
-        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_bf16"):
+        L.sage_attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, pin, i, i, i, i, f, pout, vp]
+        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_bf16", "sage_attn_fwd_int8qk"):
             getattr(L, fn).restype = i
         L.sage_status_str.argtypes, L.sage_status_str.restype = [i], ctypes.c_char_p
         _lib = L
@@ -158,6 +159,16 @@ def sage_attn_fwd_bf16(q, k, v, out, sm_scale=None, stream=None) -> None:
     st = lib().sage_attn_fwd_bf16(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D,
                                   float(sm_scale), ctypes.byref(o), _stream(stream))
     _check(st, "sage_attn_fwd_bf16")
+
+
+def sage_attn_fwd_int8qk(q_codes, q_scale, k_codes, k_scale, v, out, sm_scale=None, stream=None) -> None:
+    B, N, H, D = _shape(out)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    vi, o = bf16_in(v), bf16_out(out)
+    st = lib().sage_attn_fwd_int8qk(_ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), ctypes.byref(vi),
+                                    B, N, H, D, float(sm_scale), ctypes.byref(o), _stream(stream))
+    _check(st, "sage_attn_fwd_int8qk")
 
 
 class Buffers:

@@ -62,6 +62,16 @@ def run_attn_bf16(gcase: inputs.Case):
     return out
 
 
+def run_attn_int8qk(gcase: inputs.Case, buf=None):
+    """INT8 Q K^T (codes from sage_quantize_qk) with the bf16 V view unquantised."""
+    if buf is None:
+        buf = run_quant(gcase)
+    out = sage.token_major_out(gcase.B, gcase.N, gcase.H)
+    sage.sage_attn_fwd_int8qk(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, gcase.v, out, SM)
+    torch.cuda.synchronize()
+    return out, buf
+
+
 def out_rows(out: torch.Tensor, rows: np.ndarray) -> np.ndarray:
     """[B, N, H, D] output -> [B, H, R, D] float64 at the sampled rows."""
     o = out.float().cpu().numpy()
@@ -103,6 +113,10 @@ class OracleRef:
     def method(self, rows):
         (qc, qs), (kc, ks), (vc, vs) = self.qq, self.kq, self.vq
         return oracle.attn_method(qc, qs, kc, ks, vc, vs, SM, rows)
+
+    def int8qk(self, rows):
+        (qc, qs), (kc, ks) = self.qq, self.kq
+        return oracle.attn_int8qk(qc, qs, kc, ks, self.v, SM, rows)
 
 
 @functools.lru_cache(maxsize=5)

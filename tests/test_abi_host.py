@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_symbols_are_exported():
     names = declared_functions()
-    assert set(names) >= {"sage_quantize_qk", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_bf16",
+    assert set(names) >= {"sage_quantize_qk", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_bf16", "sage_attn_fwd_int8qk",
                           "sage_status_str", "sage_npad", "sage_qk_workspace_bytes", "sage_v_workspace_bytes"}
     L = ctypes.CDLL(sage.LIB_PATH)
     for n in names:
@@ -124,3 +124,17 @@ def test_attn_fwd_bf16_validation():
     k_bad = sage.BF16In(A, N * 3 * H * D, 64, D)
     assert L2.sage_attn_fwd_bf16(ctypes.byref(view()), ctypes.byref(k_bad), ctypes.byref(view()), B, N, H, D, 0.1,
                                  ctypes.byref(out()), None) == STRIDE
+
+
+def test_attn_fwd_int8qk_validation():
+    L = sage.lib()
+    call = lambda v=None, o=None, ptrs=(A,) * 4, sm=0.088, Dv=D: L.sage_attn_fwd_int8qk(
+        *ptrs, ctypes.byref(v or view()), B, N, H, Dv, sm, ctypes.byref(o or out()), None)
+    assert call(ptrs=(A, None, A, A)) == NULL
+    assert call(v=view(data=None)) == NULL
+    assert call(Dv=64) == SHAPE
+    assert call(ptrs=(A + 8, A, A, A)) == ALIGN
+    assert call(v=view(data=A + 2)) == ALIGN
+    assert call(v=sage.BF16In(A, N * 3 * H * D, 64, D)) == STRIDE    # V token rows overlap
+    assert call(o=out(sh=0)) == STRIDE
+    assert call(sm=float("nan")) == VALUE

@@ -230,3 +230,74 @@ def test_method_error_floor_on_gaussian_inputs():
     ref = _exact(c.q, c.k, c.v)
     err = oracle.rel_l2(got, ref)
     assert 0.02 < err < 0.06, err
+
+
+# ---------------------------------------------------- INT8 Q K^T, bf16 P.V
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Values that bf16 represents exactly, as their bf16 bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32))
+    b = t.to(torch.bfloat16)
+    assert torch.equal(b.float(), t), "values must be exact in bf16"
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_int8qk_unrounded_equals_method_on_e4m3_values():
+    # With P unrounded, the INT8-QK path with V = decoded E4M3 values (scale 1)
+    # is the quantised method with V codes and unit scales, term by term.
+    rng = np.random.default_rng(5)
+    c = inputs.hnd_case(1, 150, 2, D=128, seed=5)
+    qc, qs, kc, ks, _, _ = _quantise(c.q, c.k, c.v)
+    vc = rng.integers(0, 0x7F, size=(1, 2, 150, 128), dtype=np.uint8) | (rng.integers(0, 2, size=(1, 2, 150, 128),
+                                                                                    dtype=np.uint8) << 7)
+    vd = oracle.e4m3_decode(vc).reshape(vc.shape)                       # [B, H, N, D]
+    vview = oracle.View.from_bnhd(_bf16_bits(vd.transpose(0, 2, 1, 3)))
+    got = oracle.attn_int8qk(qc, qs, kc, ks, vview, SM, round_p=False)
+    ref = oracle.attn_method(qc, qs, kc, ks, vc, np.ones((1, 2, 128), np.float32), SM, round_p=False)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_int8qk_zero_q_gives_mean_of_v():
+    # Q = 0: every p is exactly 1 (bf16 keeps it), the output is the mean of V
+    c = inputs.hnd_case(1, 100, 2, D=128, seed=13)
+    qc, qs, kc, ks, _, _ = _quantise(c.q, c.k, c.v)
+    v = oracle_view(c.v)
+    o = oracle.attn_int8qk(np.zeros_like(qc), qs, kc, ks, v, SM)
+    vv = c.v.float().numpy().astype(np.float64).transpose(0, 2, 1, 3)   # [B, H, N, D]
+    assert np.max(np.abs(o - vv.mean(axis=2, keepdims=True))) <= 1e-14
+
+
+def test_int8qk_p_rounded_to_bf16_against_running_max_per_tile():
+    # 70 keys, D = 1: tile 0 (keys 0..63) all s = 0; tile 1 holds key 64 with s = 3
+    # and keys 65..69 with s = 0.  Tile 0's p = 1 is kept exactly (max 0); tile 1
+    # rounds p = e^-3 = 0.0497870684 to bf16 0.0498046875 (8 significant bits).
+    N = 70
+    qc = np.ones((1, 1, N, 1), np.int8); qs = np.ones((1, 1, 3), np.float32)
+    kc = np.zeros((1, 1, N, 1), np.int8); kc[0, 0, 64, 0] = 1
+    ks = np.array([[[1.0, 3.0]]], np.float32)
+    vd = np.array([0.5, 1.0, 2.0, -1.0])[np.arange(N) % 4]
+    v = oracle.View.from_bnhd(_bf16_bits(vd.reshape(1, N, 1, 1)))
+    o = oracle.attn_int8qk(qc, qs, kc, ks, v, 1.0, rows=np.zeros((1, 1, 1), np.int32))[0, 0, 0, 0]
+    a = math.exp(-3.0)
+    pb = 0.0498046875
+    assert abs(pb - a) / a < 2 ** -8
+    acc = a * vd[:64].sum() + vd[64] + pb * vd[65:].sum()
+    l = a * 64 + 1 + 5 * a
+    assert abs(o - acc / l) <= 1e-14
+    # rounding at the final maximum instead would round tile 0's p to bf16 too
+    alt = (pb * vd[:64].sum() + vd[64] + pb * vd[65:].sum()) / l
+    assert abs(o - alt) > 1e-5
+
+
+def test_int8qk_error_band_on_gaussian_inputs():
+    # INT8 Q/K with bf16 P and unquantised V: close to the exact result (the
+    # 2e-2 accuracy gate is met), far closer than the fully quantised method
+    c = inputs.config("tiny")
+    qc, qs, kc, ks, vc, vs = _quantise(c.q, c.k, c.v)
+    v = oracle_view(c.v)
+    got = oracle.attn_int8qk(qc, qs, kc, ks, v, SM)
+    unrounded = oracle.attn_int8qk(qc, qs, kc, ks, v, SM, round_p=False)
+    ref = _exact(c.q, c.k, c.v)
+    err = oracle.rel_l2(got, ref)
+    assert 5e-3 < err < 2e-2, err
+    assert oracle.rel_l2(got, unrounded) < 3e-3
+    assert err < 0.5 * oracle.rel_l2(oracle.attn_method(qc, qs, kc, ks, vc, vs, SM), ref)
