@@ -25,23 +25,18 @@
 // 64-key tile, p' = 2^(c*a - m + log2 448) ~ 448 * exp(s - m) relative to the
 // running maximum m after that tile; p' is summed in fp32 before it is rounded
 // to E4M3 for the FP8 product, and the output is acc * sv / sum(p').
-#include "sage_common.h"
+#include "sage_attn_parts.h"
 
 namespace sage {
 
 namespace {
 
-constexpr int kWaves = 4;                  // waves per workgroup
-constexpr int kQWg = 32 * kWaves;          // queries per workgroup
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTileBytes = kTile * kD;     // 8 KB per K tile and per V tile
-constexpr int kChunks = kTileBytes / 16;   // 512 16-byte chunks per tile
-constexpr float kLog2E = 1.4426950408889634f;
+using namespace attn;
+
+constexpr int kTileBytes = kI8TileBytes;   // 8 KB per K tile and per V tile
+constexpr int kChunks = kI8Chunks;         // 512 16-byte chunks per tile
 constexpr float kLog2_448 = 8.807354922057604f;
 
-// LDS slot of 16-byte chunk c (0..7) of K row r (0..63) (conflict-free for the
-// fragment reads: 32 rows x one chunk).
-__device__ __forceinline__ int k_slot(int r, int c) { return r * 8 + (c ^ ((r ^ (r >> 3)) & 7)); }
 // LDS slot of 16-byte chunk c (0..3) of V channel row d (0..127).  ds_read_b128
 // serves 16 consecutive lanes per cycle from 64 four-byte banks; with this XOR
 // the 32 channel rows x 2 chunks a fragment read touches are conflict-free
@@ -49,109 +44,34 @@ __device__ __forceinline__ int k_slot(int r, int c) { return r * 8 + (c ^ ((r ^ 
 __device__ __forceinline__ int v_swz(int d) { return (d >> 2) & 3; }
 __device__ __forceinline__ int v_slot(int d, int c) { return d * 4 + (c ^ v_swz(d)); }
 
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// v_permlane32_swap exchanges the upper half-wave of its first operand with the
-// lower half-wave of its second.  With both operands x, one result holds x of
-// lanes 0..31 in every lane position l % 32 and the other x of lanes 32..63, so
-// combining the two gives every lane the value of its pair (l, l ^ 32).
-__device__ __forceinline__ int pair_max(int x) {
-    auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return max((int)r[0], (int)r[1]);
-}
-__device__ __forceinline__ float pair_sum(float x) {
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
-
-// Direct HBM -> LDS staging (buffer_load_dwordx4 ... lds): lane L of a wave's
-// load instruction writes LDS bytes [16 L, 16 L + 16) after the instruction's
-// LDS base, so each lane fetches the global chunk that belongs at its
-// (swizzled) LDS slot.  Wave w issues slots [128 w, 128 w + 128) of each
-// 512-slot tile.  The per-lane byte offsets are loop invariant; the tile base
-// lives in a buffer descriptor (scalar registers) whose 8 KB record limit also
-// bounds every access to the tile.
-typedef __attribute__((address_space(3))) void lds_void;
-
+// HBM -> LDS staging of the K tile (shared INT8 loader) and of the tile-major
+// V codes: wave w fills slots [128 w, 128 w + 128) of the 512-slot V tile, lane
+// L of load i slot 128 w + 64 i + L, from the per-lane source offsets below.
 struct TileLoader {
-    int koff[2], voff[2];   // per-lane source byte offsets within a K tile and a V tile
+    K8Loader k;
+    int voff[2];
 };
 
 __device__ __forceinline__ TileLoader make_loader(int w, int lane) {
     TileLoader L;
+    L.k = make_k8_loader(w, lane);
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int slot = 128 * w + 64 * i + lane;
-        const int r = slot >> 3, rc = slot & 7;                  // K: LDS slot -> row, stored chunk
-        L.koff[i] = r * 128 + 16 * (rc ^ ((r ^ (r >> 3)) & 7));
-        const int d = slot >> 2, dc = slot & 3;                  // V: LDS slot -> channel, stored chunk
+        const int d = slot >> 2, dc = slot & 3;   // LDS slot -> channel, stored chunk
         L.voff[i] = d * 64 + 16 * (dc ^ v_swz(d));
     }
     return L;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void *tile) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(tile), 0, kTileBytes, 0x00020000);
-}
-
 __device__ __forceinline__ void lds_load_k(v4i *lk, const int8_t *tile, const TileLoader &L, int w) {
-    const auto r = tile_rsrc(tile);
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lk + 128 * w + 64 * i), 16, L.koff[i], 0, 0, 0);
+    lds_load_k8(lk, tile, L.k, w);
 }
 __device__ __forceinline__ void lds_load_v(v4i *lv, const uint8_t *tile, const TileLoader &L, int w) {
-    const auto r = tile_rsrc(tile);
+    const auto r = tile_rsrc(tile, kTileBytes);
 #pragma unroll
     for (int i = 0; i < 2; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lv + 128 * w + 64 * i), 16, L.voff[i], 0, 0, 0);
-}
-// Wait for this wave's outstanding HBM -> LDS loads (vmcnt = 0), then the
-// barrier.  The scheduling fences keep register-only work of neighbouring steps
-// from drifting across it, so each step keeps its MFMA/VALU interleave.
-__device__ __forceinline__ void wait_lds_loads_and_sync() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unchanged
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-// S^T = K Q^T for one 64-key tile: two 32-key blocks, four 32-channel k-steps.
-// Lane (hl, ql) register r of block kb holds key 32*kb + 8*(r/4) + 4*hl + r%4.
-// MFMA i (0..7) is block i%2, k-step i/2: the two accumulation chains
-// alternate, so no MFMA waits on the one issued just before it.
-__device__ __forceinline__ void qk_mfma(const v4i *lk, const v4i (&qa)[4], int hl, int ql, v16i (&s)[2], int i) {
-    const int kb = i & 1, st = i >> 1;
-    v4i ka = lk[k_slot(32 * kb + ql, 2 * st + hl)];
-    s[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qa[st], st ? s[kb] : v16i{}, 0, 0, 0);
-}
-
-__device__ __forceinline__ void qk_tile(const v4i *lk, const v4i (&qa)[4], int hl, int ql, v16i (&s)[2]) {
-#pragma unroll
-    for (int i = 0; i < 8; i++) qk_mfma(lk, qa, hl, ql, s, i);
-}
-
-// Running maximum after one tile, from its int32 scores (log2 units; c2 >= 0 so
-// the maximum of c2 * a is c2 * max a).  TAIL first masks keys >= nvalid.
-template <bool TAIL>
-__device__ __forceinline__ float tile_max(v16i (&s)[2], float c2, int nvalid, int hl, float m2) {
-    if (TAIL) {
-#pragma unroll
-        for (int kb = 0; kb < 2; kb++)
-#pragma unroll
-            for (int r = 0; r < 16; r++)
-                if (32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3) >= nvalid) s[kb][r] = INT32_MIN;
-    }
-    // a chain of 3-input maxima: 16 v_max3_i32 for 32 values
-    int imax = max(max(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-    for (int r = 3; r < 15; r += 2) imax = max(max(imax, s[0][r]), s[0][r + 1]);
-    imax = max(max(imax, s[0][15]), s[1][0]);
-#pragma unroll
-    for (int r = 1; r < 15; r += 2) imax = max(max(imax, s[1][r]), s[1][r + 1]);
-    imax = max(imax, s[1][15]);
-    imax = pair_max(imax);
-    return fmaxf(m2, c2 * (float)imax);
 }
 
 // p' = 448 * exp(s - m) for registers 4c..4c+3 of the tile (c = 0..7), summed
@@ -185,21 +105,7 @@ __device__ __forceinline__ void pv_tile(const v4i *lv, const v8i &pf, int hl, in
     }
 }
 
-__device__ __forceinline__ void rescale(float alpha, v16f (&o)[4]) {
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {   // wave-uniform; skip when no max moved
-#pragma unroll
-        for (int db = 0; db < 4; db++)
-#pragma unroll
-            for (int r = 0; r < 16; r++) o[db][r] *= alpha;
-    }
-}
-
-// MFMA operands read from LDS: K fragment i (block i%2, k-step i/2) of a tile and
-// the V fragment of channel block db.
-__device__ __forceinline__ v4i k_operand(const v4i *lk, int i, int hl, int ql) {
-    const int kb = i & 1, st = i >> 1;
-    return lk[k_slot(32 * kb + ql, 2 * st + hl)];
-}
+// FP8 MFMA operand of channel block db, read from the tile-major V codes in LDS.
 __device__ __forceinline__ v8i v_operand(const v4i *lv, int db, int hl, int ql) {
     const int d = 32 * db + ql;
     v4i lo = lv[v_slot(d, 2 * hl)];
@@ -232,18 +138,18 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
     v4i ka[3];
     if (PV) va[0] = v_operand(lv_prev, 0, hl, ql);
     else if (QK) {
-        ka[0] = k_operand(lk_next, 0, hl, ql);
-        ka[1] = k_operand(lk_next, 1, hl, ql);
+        ka[0] = k8_operand(lk_next, 0, hl, ql);
+        ka[1] = k8_operand(lk_next, 1, hl, ql);
     }
     if (PV) {   // O = alpha(t-1) acc(t-2) + P(t-1) V(t-1)
 #pragma unroll
         for (int db = 0; db < 4; db++) {
             if (db < 3) va[(db + 1) & 1] = v_operand(lv_prev, db + 1, hl, ql);
-            if (QK && db >= 2) ka[db - 2] = k_operand(lk_next, db - 2, hl, ql);
+            if (QK && db >= 2) ka[db - 2] = k8_operand(lk_next, db - 2, hl, ql);
             o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db & 1], st.pf, o[db], 0, 0, 0, 127, 0, 127);
         }
     }
-    const float mnew = tile_max<TAIL>(s, c2, nvalid, hl, st.m2);
+    const float mnew = tile_max_i32<TAIL>(s, c2, nvalid, hl, st.m2);
     const float alpha = fast_exp2(st.m2 - mnew);   // 0 on the first tile (m2 = -inf)
     st.m2 = mnew;
     const float bias = mnew - kLog2_448;
@@ -251,7 +157,7 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
 #pragma unroll
     for (int c = 0; c < 8; c++) {
         if (QK) {
-            if (c < 6) ka[(c + 2) % 3] = k_operand(lk_next, c + 2, hl, ql);
+            if (c < 6) ka[(c + 2) % 3] = k8_operand(lk_next, c + 2, hl, ql);
             const int kb = c & 1, kst = c >> 1;   // the two accumulation chains alternate
             sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[c % 3], qa[kst], kst ? sn[kb] : v16i{}, 0, 0, 0);
         }
@@ -337,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
     if (ntiles > 1) lds_load_k(lk1, kbase + kTileBytes, ldr, w);
     wait_lds_loads_and_sync();
     v16i sa[2], sb[2];
-    qk_tile(lk0, qa, hl, ql, sa);
+    qk8_tile(lk0, qa, hl, ql, sa);
     __syncthreads();
 
     // Step t stages K(t+2) and V(t) into the buffers of K(t) and V(t-2), which
