@@ -83,20 +83,43 @@ template <bool PV, bool QK, bool TAIL>
 __device__ __forceinline__ void step(v16f (&s)[2], v16f (&sn)[2], const v4i *lk_next, const v4i *lv_prev,
                                      const v8bf (&qa)[8], float c2, int nvalid, int lane, int hl, int ql,
                                      RowState &st, v16f (&o)[4]) {
-    if (PV) pv16_tile(lv_prev, st.pw, lane, o);
+    // P.V MFMA j (0..15) = k-step j / 4, channel block j % 4.  Six of them run
+    // beside the max reduction, the rest two per exp chunk (chunks 0..4), each
+    // before the chunk that first overwrites its k-step of the P operand.
+    v8bf pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        pb[ks] = __builtin_bit_cast(v8bf, make_uint4(st.pw[4 * ks], st.pw[4 * ks + 1], st.pw[4 * ks + 2],
+                                                     st.pw[4 * ks + 3]));
+    auto pv = [&](int j) {
+        const int ks = j >> 2, db = j & 3;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v16_operand(lv_prev, lane, ks, db), pb[ks], o[db], 0, 0, 0);
+    };
+    if (PV) {
+#pragma unroll
+        for (int j = 0; j < 6; j++) pv(j);
+    }
     const float mnew = tile_max<TAIL>(s, c2, nvalid, hl, st.m2);
     const float alpha = fast_exp2(st.m2 - mnew);
     st.m2 = mnew;
     float part = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 8; c++) {
         if (QK) {
             qk_mfma(lk_next, qa, hl, ql, sn, 2 * c);
             qk_mfma(lk_next, qa, hl, ql, sn, 2 * c + 1);
         }
+        if (PV && c < 5) {
+            pv(6 + 2 * c);
+            pv(7 + 2 * c);
+        }
         tile_exp_chunk<TAIL>(s, c2, mnew, nvalid, hl, c, st.pw, part);
+        asm volatile("" ::"v"(part));
+        __builtin_amdgcn_sched_barrier(0);
     }
-    asm volatile("" ::"v"(st.pw[0]), "v"(st.pw[4]), "v"(st.pw[8]), "v"(st.pw[12]), "v"(part));
+#pragma unroll
+    for (int i = 0; i < 16; i++) asm volatile("" ::"v"(st.pw[i]));
     if (QK) asm volatile("" ::"v"(sn[0]), "v"(sn[1]));
     __builtin_amdgcn_sched_barrier(0);
     st.lsum = st.lsum * alpha + part;

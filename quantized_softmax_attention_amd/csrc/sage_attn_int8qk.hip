@@ -48,23 +48,40 @@ __device__ __forceinline__ void tile_exp_chunk(const v16i (&s)[2], float c2, flo
     pw[4 * ks + (e0 >> 1) + 1] = pack_bf16(p[2], p[3]);
 }
 
-// One pipeline step for tile t: P.V of tile t-1 (16 bf16 MFMAs), the running
-// maximum and p of tile t with the 8 INT8 QK^T MFMAs of tile t+1 interleaved,
-// then the rescale of O (a branch, taken only when some row's maximum moved).
+// One pipeline step for tile t: P.V of tile t-1 (16 bf16 MFMAs, spread over the
+// step), the running maximum and p of tile t with the 8 INT8 QK^T MFMAs of tile
+// t+1 interleaved, then the rescale of O (a branch, taken only when some row's
+// maximum moved).
 template <bool PV, bool QK, bool TAIL>
 __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_next, const v4i *lv_prev,
                                      const v4i (&qa)[4], float c2, int nvalid, int lane, int hl, int ql,
                                      RowState &st, v16f (&o)[4]) {
+    // P.V MFMA j (0..15) = k-step j / 4, channel block j % 4.  Six of them run
+    // beside the max reduction, the rest two per exp chunk (chunks 0..4), each
+    // before the chunk that first overwrites its k-step of the P operand.
+    v8bf pb[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++)
+        pb[ks] = __builtin_bit_cast(v8bf, make_uint4(st.pw[4 * ks], st.pw[4 * ks + 1], st.pw[4 * ks + 2],
+                                                     st.pw[4 * ks + 3]));
+    auto pv = [&](int j) {
+        const int ks = j >> 2, db = j & 3;
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v16_operand(lv_prev, lane, ks, db), pb[ks], o[db], 0, 0, 0);
+    };
     v4i ka[3];
     if (QK) {
         ka[0] = k8_operand(lk_next, 0, hl, ql);
         ka[1] = k8_operand(lk_next, 1, hl, ql);
     }
-    if (PV) pv16_tile(lv_prev, st.pw, lane, o);   // O = alpha(t-1) acc(t-2) + P(t-1) V(t-1)
+    if (PV) {   // O = alpha(t-1) acc(t-2) + P(t-1) V(t-1), first six MFMAs
+#pragma unroll
+        for (int j = 0; j < 6; j++) pv(j);
+    }
     const float mnew = tile_max_i32<TAIL>(s, c2, nvalid, hl, st.m2);
     const float alpha = fast_exp2(st.m2 - mnew);   // 0 on the first tile (m2 = -inf)
     st.m2 = mnew;
     float part = 0.0f;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 8; c++) {
         if (QK) {
@@ -72,7 +89,13 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
             const int kb = c & 1, kst = c >> 1;
             sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka[c % 3], qa[kst], kst ? sn[kb] : v16i{}, 0, 0, 0);
         }
+        if (PV && c < 5) {
+            pv(6 + 2 * c);
+            pv(7 + 2 * c);
+        }
         tile_exp_chunk<TAIL>(s, c2, mnew, nvalid, hl, c, st.pw, part);
+        asm volatile("" ::"v"(part));
+        __builtin_amdgcn_sched_barrier(0);
     }
     // Everything above is consumed only after the rescale branch; reading it
     // here keeps it (and the MFMAs) inside this step's schedule.
