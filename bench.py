@@ -65,19 +65,27 @@ def attn_bytes(b=B, n=N, h=H, d=D) -> int:
     return 3 * b * h * npad * d + 2 * b * n * h * d
 
 
-def source_hash(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+CSRC = os.path.join(ROOT, "quantized_softmax_attention_amd", "csrc")
+# the sources the fused attention kernel is compiled from
+ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("sage_attn.hip", "sage_attn_parts.h", "sage_common.h")]
 
 
-def load_traffic(kernel_src: str):
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
     """Measured HBM traffic of the attention kernel from committed counter runs,
-    only if they were taken on the current kernel source."""
+    only if they were taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "attn_i8f8_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_source_sha256_16") != source_hash(kernel_src):
+    if rec.get("kernel_source_sha256_16") != source_hash(ATTN_SOURCES):
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -207,7 +215,6 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     attn_mean = statistics.fmean(at_ms)
     achieved = flops / (attn_mean * 1e-3) / 1e12
-    kernel_src = os.path.join(ROOT, "quantized_softmax_attention_amd", "csrc", "sage_attn.hip")
     qb = quant_bytes()
 
     # the bf16 comparison path on the same resident inputs
@@ -249,7 +256,7 @@ def main():
                    "B": B, "N": N, "H": H, "D": D, "layout": "strided_nhd", "non_causal": True},
         "roofline": {"bound": "mfma", "kernel": "attn_i8f8_kernel", "achieved": achieved,
                      "peak": PEAK_I8F8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_I8F8_TFLOPS,
-                     "traffic": load_traffic(kernel_src), "algorithmic_bytes": attn_bytes(),
+                     "traffic": load_traffic(), "algorithmic_bytes": attn_bytes(),
                      "flops_per_launch": flops, "ms_per_launch": attn_mean},
         "stages": {
             "qk_quantize_ms": stats_ms(qk_ms), "v_quantize_ms": stats_ms(v_ms), "attn_fwd_ms": stats_ms(at_ms),

@@ -52,7 +52,7 @@ def test_attn_parity_workloads(name):
     _gate(G.out_rows(out, rows), ref, rows, name)
 
 
-@pytest.mark.parametrize("N", [1, 2, 31, 33, 63, 64, 65, 127, 128, 129, 255, 257, 1000])
+@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257, 1000])
 def test_attn_parity_ragged(N):
     print("attention parity ragged N =", N, flush=True)
     case = inputs.packed_case(2, N, 2, seed=100 + N, stress=(N % 2 == 0))
@@ -67,6 +67,16 @@ def test_attn_parity_ragged(N):
         from oracle import e4m3_decode
         v0 = e4m3_decode(vc[:, :, 0]).reshape(vc[:, :, 0].shape) * vs
         assert np.allclose(got[:, :, 0], v0, rtol=2 ** -8, atol=0)
+
+
+@pytest.mark.parametrize("B,N,H", [(1, 4095, 1), (2, 300, 1)])
+def test_attn_parity_single_head(B, N, H):
+    print("attention parity B=%d N=%d H=%d" % (B, N, H), flush=True)
+    case = inputs.packed_case(B, N, H, seed=400 + N)
+    ref = G.OracleRef(case)
+    out, _ = G.run_attn(G.gpu_case(case))
+    rows = _rows(case, (256, 64) if N > 512 else None)
+    _gate(G.out_rows(out, rows), ref, rows, "B=%d N=%d H=%d" % (B, N, H))
 
 
 def test_attn_zero_q_gives_mean_of_dequantised_v():
