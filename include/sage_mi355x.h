@@ -130,6 +130,23 @@ int sage_quantize_v(const sage_bf16_in *v, int B, int N, int H, int D,
                     uint8_t *v_codes, float *v_scale, void *workspace, size_t workspace_bytes,
                     void *stream);
 
+/* Bytes of device workspace sage_quantize_qkv needs: ceil(N/64)*B*H*D doubles
+ * (K-mean chunk partials) plus ceil(N/64)*B*H*D floats (per-64-token channel
+ * maxima of |V|) plus B*H*D floats. */
+size_t sage_qkv_workspace_bytes(int B, int N, int H, int D);
+
+/* sage_quantize_qk and sage_quantize_v in one call: the same outputs, bit for
+ * bit, from three passes over the inputs instead of six (one pass gathers the K
+ * smoothing statistic, the V channel maxima and the Q codes; the last writes the
+ * K and V codes).  This folds the profile page's
+ * framework_and_k_smoothing_estimate into the quantisation passes.  Arguments,
+ * layouts and alignment as the two calls; workspace >=
+ * sage_qkv_workspace_bytes(B, N, H, D) bytes, 8-byte aligned. */
+int sage_quantize_qkv(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N, int H,
+                      int D, int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale,
+                      float *k_mean, uint8_t *v_codes, float *v_scale, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* attention_forward (profile page, attention_internal_p50_milliseconds.sage2
  * .attention_forward; latency page, the whole artefact): from the buffers the two
  * calls above wrote, for every query i < N of every (b, h):

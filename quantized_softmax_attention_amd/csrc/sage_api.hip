@@ -11,6 +11,8 @@ hipError_t launch_quantize_qk(View q, View k, int B, int N, int H, int8_t *qc, f
                               float *ks, float *km, void *workspace, hipStream_t stream);
 hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs, void *workspace,
                              hipStream_t stream);
+hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, int8_t *qc, float *qs, int8_t *kc,
+                               float *ks, float *km, uint8_t *vc, float *vs, void *workspace, hipStream_t stream);
 hipError_t launch_attn_fwd(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
                            const float *vs, int B, int N, int H, float sm_scale, OutView out, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(View q, View k, View v, int B, int N, int H, float sm_scale, OutView out,
@@ -110,6 +112,13 @@ size_t sage_v_workspace_bytes(int B, int N, int H, int D) {
     return (nchunk + 1) * (size_t)B * H * D * sizeof(float);
 }
 
+size_t sage_qkv_workspace_bytes(int B, int N, int H, int D) {
+    if (check_shape(B, N, H, D) != SAGE_OK) return 0;
+    const size_t nchunk = (size_t)((N + SAGE_K_BLOCK - 1) / SAGE_K_BLOCK);
+    const size_t total = (size_t)B * H * D;
+    return nchunk * total * (sizeof(double) + sizeof(float)) + total * sizeof(float);
+}
+
 int sage_quantize_qk(const sage_bf16_in *q, const sage_bf16_in *k, int B, int N, int H, int D, int8_t *q_codes,
                      float *q_scale, int8_t *k_codes, float *k_scale, float *k_mean, void *workspace,
                      size_t workspace_bytes, void *stream) {
@@ -135,6 +144,23 @@ int sage_quantize_v(const sage_bf16_in *v, int B, int N, int H, int D, uint8_t *
     if (workspace_bytes < sage_v_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
     return hip_status(sage::launch_quantize_v(to_view(v), B, N, H, v_codes, v_scale, workspace,
                                               static_cast<hipStream_t>(stream)));
+}
+
+int sage_quantize_qkv(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N, int H,
+                      int D, int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale, float *k_mean,
+                      uint8_t *v_codes, float *v_scale, void *workspace, size_t workspace_bytes, void *stream) {
+    int st;
+    if ((st = check_in(q)) || (st = check_in(k)) || (st = check_in(v))) return st;
+    if (!q_codes || !q_scale || !k_codes || !k_scale || !k_mean || !v_codes || !v_scale || !workspace)
+        return SAGE_ERR_NULL;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4) || !aligned(workspace, 8))
+        return SAGE_ERR_ALIGN;
+    if (workspace_bytes < sage_qkv_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
+    return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, q_codes, q_scale,
+                                                k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int sage_attn_fwd(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes, const float *k_scale,

@@ -63,6 +63,15 @@ __global__ __launch_bounds__(256) void kmean_final_kernel(const double *__restri
     km[i] = (float)(s / (double)N);
 }
 
+// 8 consecutive channels of one token row (a 16-byte load), widened exactly.
+__device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (&x)[8]) {
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (valid) raw = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int j = 0; j < 8; j++) x[j] = bf16_to_f32((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+}
+
 // ------------------------------------------------------------- INT8 blocks
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -77,76 +86,108 @@ __device__ __forceinline__ uint32_t int8_code(float x, float scale) {
     return (uint32_t)((int32_t)r) & 0xFFu;
 }
 
+// Workgroup-wide maxima of M per-thread values (256 threads, 4 waves) with one
+// barrier pair; red is M x 4 floats of LDS.  Every thread gets every maximum.
+template <int M>
+__device__ __forceinline__ void block_maxes(float (&m)[M], float (*red)[4]) {
+#pragma unroll
+    for (int i = 0; i < M; i++) m[i] = wave_max(m[i]);
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int i = 0; i < M; i++) red[i][threadIdx.x >> 6] = m[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < M; i++) m[i] = fmaxf(fmaxf(red[i][0], red[i][1]), fmaxf(red[i][2], red[i][3]));
+    __syncthreads();
+}
+
+// The INT8 blocks of one 64-token block tb of one head, thread t holding
+// channels 8*(t%16)..+7 of tokens t/16 + 16*i, i = 0..3 (x, already widened;
+// tokens >= N hold zeros, which changes no block maximum and yields zero
+// codes).  Q: two 32-token blocks (i < 2 and i >= 2); K: one 64-token block.
+__device__ __forceinline__ void q_local_max(const float (&x)[4][8], float &m0, float &m1) {
+    m0 = 0.0f;
+    m1 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            if (i < 2) m0 = fmaxf(m0, fabsf(x[i][j]));
+            else m1 = fmaxf(m1, fabsf(x[i][j]));
+        }
+}
+__device__ __forceinline__ float k_local_max(const float (&x)[4][8]) {
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 8; j++) m = fmaxf(m, fabsf(x[i][j]));
+    return m;
+}
+
+// Codes of the thread's 4 x 8 values with scale sc(i) for token row i.
+__device__ __forceinline__ void store_int8_codes(const float (&x)[4][8], float s_lo, float s_hi, int tb, int64_t bh,
+                                                 int64_t Npad, int8_t *__restrict__ codes) {
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const float sc = i < 2 ? s_lo : s_hi;
+        uint32_t c[2] = {0, 0};
+#pragma unroll
+        for (int j = 0; j < 8; j++) c[j >> 2] |= int8_code(x[i][j], sc) << (8 * (j & 3));
+        const int64_t off = (bh * Npad + (int64_t)tb * 64 + row + 16 * i) * kD + seg * 8;
+        *reinterpret_cast<uint2 *>(codes + off) = make_uint2(c[0], c[1]);
+    }
+}
+
+// K of the block, smoothed: x = fp32(k) - k_mean (one fp32 subtraction); zero
+// for tokens >= N.
+__device__ __forceinline__ void load_k_smoothed(View k, int b, int h, int tb, int N, const float *__restrict__ km,
+                                                int64_t bh, float (&x)[4][8]) {
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
+    float mean[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) mean[j] = km[bh * kD + seg * 8 + j];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        load_row8(kb + (int64_t)n * k.sn, n < N, x[i]);
+#pragma unroll
+        for (int j = 0; j < 8; j++) x[i][j] = n < N ? x[i][j] - mean[j] : 0.0f;
+    }
+}
+
+__device__ __forceinline__ void load_block(View a, int b, int h, int tb, int N, float (&x)[4][8]) {
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const uint16_t *base = a.data + (int64_t)b * a.sb + (int64_t)h * a.sh + seg * 8;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        load_row8(base + (int64_t)n * a.sn, n < N, x[i]);
+    }
+}
+
 // One workgroup per (64-token block tb, head h, batch b): two Q blocks of 32
-// tokens and one K block of 64.  Thread t holds channels 8*(t%16)..+7 of tokens
-// t/16 + 16*i, i = 0..3.  Tokens >= N load as zero, which changes no block
-// maximum and yields zero codes, so padded rows need no special case.
+// tokens and one K block of 64.
 __global__ __launch_bounds__(256) void quant_qk_kernel(View q, View k, int N, int H, int64_t Npad,
                                                        const float *__restrict__ km,
                                                        int8_t *__restrict__ qc, float *__restrict__ qs,
                                                        int8_t *__restrict__ kc, float *__restrict__ ks) {
     __shared__ float red[3][4];
     const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int t = threadIdx.x, row = t >> 4, seg = t & 15, lane = t & 63, wave = t >> 6;
     const int64_t bh = (int64_t)b * H + h;
-    const uint16_t *qb = q.data + (int64_t)b * q.sb + (int64_t)h * q.sh + seg * 8;
-    const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
-    float mean[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) mean[j] = km[bh * kD + seg * 8 + j];
-
     float xq[4][8], xk[4][8];
-    float mq0 = 0.0f, mq1 = 0.0f, mk = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int n = tb * 64 + row + 16 * i;
-        uint4 rq = make_uint4(0, 0, 0, 0), rk = make_uint4(0, 0, 0, 0);
-        bool valid = n < N;
-        if (valid) {
-            rq = *reinterpret_cast<const uint4 *>(qb + (int64_t)n * q.sn);
-            rk = *reinterpret_cast<const uint4 *>(kb + (int64_t)n * k.sn);
-        }
-        uint32_t wq[4] = {rq.x, rq.y, rq.z, rq.w}, wk[4] = {rk.x, rk.y, rk.z, rk.w};
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            uint32_t bq = (j & 1) ? (wq[j >> 1] >> 16) : (wq[j >> 1] & 0xFFFFu);
-            uint32_t bk = (j & 1) ? (wk[j >> 1] >> 16) : (wk[j >> 1] & 0xFFFFu);
-            xq[i][j] = bf16_to_f32(bq);
-            xk[i][j] = valid ? bf16_to_f32(bk) - mean[j] : 0.0f;
-            if (i < 2) mq0 = fmaxf(mq0, fabsf(xq[i][j]));
-            else mq1 = fmaxf(mq1, fabsf(xq[i][j]));
-            mk = fmaxf(mk, fabsf(xk[i][j]));
-        }
-    }
-    mq0 = wave_max(mq0);
-    mq1 = wave_max(mq1);
-    mk = wave_max(mk);
-    if (lane == 0) {
-        red[0][wave] = mq0;
-        red[1][wave] = mq1;
-        red[2][wave] = mk;
-    }
-    __syncthreads();
-    float aq0 = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
-    float aq1 = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
-    float ak = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
-    float sq0 = aq0 / 127.0f, sq1 = aq1 / 127.0f, sk = ak / 127.0f;
-
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        int64_t n = (int64_t)tb * 64 + row + 16 * i;
-        float sq = i < 2 ? sq0 : sq1;
-        uint32_t cq[2] = {0, 0}, ck[2] = {0, 0};
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            cq[j >> 2] |= int8_code(xq[i][j], sq) << (8 * (j & 3));
-            ck[j >> 2] |= int8_code(xk[i][j], sk) << (8 * (j & 3));
-        }
-        int64_t off = (bh * Npad + n) * kD + seg * 8;
-        *reinterpret_cast<uint2 *>(qc + off) = make_uint2(cq[0], cq[1]);
-        *reinterpret_cast<uint2 *>(kc + off) = make_uint2(ck[0], ck[1]);
-    }
-    if (t == 0) {
+    load_block(q, b, h, tb, N, xq);
+    load_k_smoothed(k, b, h, tb, N, km, bh, xk);
+    float m[3];
+    q_local_max(xq, m[0], m[1]);
+    m[2] = k_local_max(xk);
+    block_maxes(m, red);
+    const float sq0 = m[0] / 127.0f, sq1 = m[1] / 127.0f, sk = m[2] / 127.0f;
+    store_int8_codes(xq, sq0, sq1, tb, bh, Npad, qc);
+    store_int8_codes(xk, sk, sk, tb, bh, Npad, kc);
+    if (threadIdx.x == 0) {
         qs[bh * (Npad / kQBlock) + 2 * tb] = sq0;
         qs[bh * (Npad / kQBlock) + 2 * tb + 1] = sq1;
         ks[bh * (Npad / kKBlock) + tb] = sk;
@@ -209,19 +250,16 @@ __global__ __launch_bounds__(256) void v_amax_final_kernel(const float *__restri
     vs[i] = a / 448.0f;
 }
 
-// One workgroup per (64-key tile t, head h, batch b).  Thread (g = tid/16,
-// seg = tid%16) encodes keys 4g..4g+3 of channels 8*seg..+7.  The four codes
-// of one channel land in consecutive bytes p0..p0+3 of the tile row, where p0
-// inverts kappa (see the public header): keys 4g..4g+3 sit at
+// The E4M3 codes of one 64-key tile tt of one head, written tile-major.  Thread
+// (g = tid/16, seg = tid%16) encodes keys 4g..4g+3 of channels 8*seg..+7.  The
+// four codes of one channel land in consecutive bytes p0..p0+3 of the tile row,
+// where p0 inverts kappa (see the public header): keys 4g..4g+3 sit at
 // p0 = 32*(g%2) + 16*(g/8) + 4*((g/2)%4).  The 8 KB tile is assembled in LDS
-// and written out with coalesced 16-byte stores.
-__global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int64_t Npad,
-                                                      const float *__restrict__ vs,
-                                                      uint8_t *__restrict__ vc) {
-    __shared__ uint32_t tile[kD][kTile / 4];
-    const int tt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+// (tile: kD x 16 words) and written out with coalesced 16-byte stores.
+__device__ __forceinline__ void v_tile_codes(View v, int b, int h, int tt, int N, int64_t bh, int64_t Npad,
+                                             const float *__restrict__ vs, uint8_t *__restrict__ vc,
+                                             uint32_t (*tile)[kTile / 4]) {
     const int t = threadIdx.x, g = t >> 4, seg = t & 15;
-    const int64_t bh = (int64_t)b * H + h;
     const uint16_t *base = v.data + (int64_t)b * v.sb + (int64_t)h * v.sh + seg * 8;
     float sv[8];
 #pragma unroll
@@ -229,14 +267,12 @@ __global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int6
     uint32_t packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        int n = tt * kTile + 4 * g + i;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (n < N) raw = *reinterpret_cast<const uint4 *>(base + (int64_t)n * v.sn);
-        uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        const int n = tt * kTile + 4 * g + i;
+        float x[8];
+        load_row8(base + (int64_t)n * v.sn, n < N, x);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            uint32_t bits = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-            uint32_t code = (sv[j] == 0.0f || n >= N) ? 0u : e4m3_encode(bf16_to_f32(bits) / sv[j]);
+            const uint32_t code = (sv[j] == 0.0f || n >= N) ? 0u : e4m3_encode(x[j] / sv[j]);
             packed[j] |= code << (8 * i);
         }
     }
@@ -248,6 +284,134 @@ __global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int6
     const uint4 *src = reinterpret_cast<const uint4 *>(&tile[0][0]);
     dst[t] = src[t];
     dst[t + 256] = src[t + 256];
+}
+
+// One workgroup per (64-key tile tt, head h, batch b).
+__global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int64_t Npad,
+                                                      const float *__restrict__ vs,
+                                                      uint8_t *__restrict__ vc) {
+    __shared__ uint32_t tile[kD][kTile / 4];
+    const int tt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    v_tile_codes(v, b, h, tt, N, (int64_t)b * H + h, Npad, vs, vc, tile);
+}
+
+// ------------------------------------------------- Q, K and V in one call
+// The same results as quantize_qk + quantize_v in three passes instead of six:
+//   1. per (64-token block, head, batch): the Q codes and scales, the K-mean
+//      chunk partial (fp64, per channel, tokens in ascending order) and the
+//      block's per-channel max |V|;
+//   2. per (b, h, d): k_mean (chunk partials in ascending order, / N) and the V
+//      channel maximum and scale;
+//   3. per (64-token block, head, batch): the K codes and scale (smoothed) and
+//      the block's V codes.
+__global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, int N, int H, int64_t Npad,
+                                                        int nchunk, int8_t *__restrict__ qc,
+                                                        float *__restrict__ qs, double *__restrict__ wsk,
+                                                        float *__restrict__ wsv) {
+    __shared__ float red[2][4];
+    __shared__ uint4 kbuf[kKBlock][kD / 8];      // the block's K rows, bf16 (16 KB)
+    __shared__ float vred[16][kD + 4];
+    const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const int64_t bh = (int64_t)b * H + h;
+    // K and V rows (raw) of this thread: tokens row + 16 i; tokens >= N read as zero
+    const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
+    const uint16_t *vb = v.data + (int64_t)b * v.sb + (int64_t)h * v.sh + seg * 8;
+    float vm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        uint4 rk = make_uint4(0, 0, 0, 0);
+        if (n < N) rk = *reinterpret_cast<const uint4 *>(kb + (int64_t)n * k.sn);
+        kbuf[row + 16 * i][seg] = rk;
+        float xv[8];
+        load_row8(vb + (int64_t)n * v.sn, n < N, xv);
+#pragma unroll
+        for (int j = 0; j < 8; j++) vm[j] = fmaxf(vm[j], fabsf(xv[j]));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j++) vred[row][seg * 8 + j] = vm[j];
+    float xq[4][8];
+    load_block(q, b, h, tb, N, xq);
+    float m[2];
+    q_local_max(xq, m[0], m[1]);
+    block_maxes(m, red);                             // its barriers also publish kbuf and vred
+    const float sq0 = m[0] / 127.0f, sq1 = m[1] / 127.0f;
+    store_int8_codes(xq, sq0, sq1, tb, bh, Npad, qc);
+    if (t == 0) {
+        qs[bh * (Npad / kQBlock) + 2 * tb] = sq0;
+        qs[bh * (Npad / kQBlock) + 2 * tb + 1] = sq1;
+    }
+    if (tb >= nchunk) return;                        // a padding block: zero Q codes only
+    if (t < kD) {
+        // channel t summed over the block's tokens in ascending order (zeros past N
+        // change no fp64 sum)
+        const uint16_t *col = reinterpret_cast<const uint16_t *>(&kbuf[0][0]) + t;
+        double sum = 0.0;
+#pragma unroll 16
+        for (int r = 0; r < kKBlock; r++) sum += (double)bf16_to_f32(col[r * kD]);
+        wsk[(((int64_t)b * nchunk + tb) * H + h) * kD + t] = sum;
+    } else {
+        const int d = t - kD;
+        float a = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; r++) a = fmaxf(a, vred[r][d]);
+        wsv[(((int64_t)b * nchunk + tb) * H + h) * kD + d] = a;
+    }
+}
+
+// k_mean and the V channel maxima and scales from the pass-1 partials.
+__global__ __launch_bounds__(256) void qkv_final_kernel(const double *__restrict__ wsk, const float *__restrict__ wsv,
+                                                        int N, int H, int nchunk, int B, float *__restrict__ km,
+                                                        float *__restrict__ amax, float *__restrict__ vs) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t HD = (int64_t)H * kD;
+    if (i >= (int64_t)B * HD) return;
+    const int64_t b = i / HD, hd = i % HD;
+    const double *pk = wsk + b * nchunk * HD + hd;
+    const float *pv = wsv + b * nchunk * HD + hd;
+    double s = 0.0;
+    float a = 0.0f;
+    int c = 0;
+    for (; c + 16 <= nchunk; c += 16) {   // loads issued 16 at a time ahead of the ordered adds
+        double x[16];
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            x[j] = pk[(int64_t)(c + j) * HD];
+            y[j] = pv[(int64_t)(c + j) * HD];
+        }
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            s += x[j];
+            a = fmaxf(a, y[j]);
+        }
+    }
+    for (; c < nchunk; c++) {
+        s += pk[(int64_t)c * HD];
+        a = fmaxf(a, pv[(int64_t)c * HD]);
+    }
+    km[i] = (float)(s / (double)N);
+    amax[i] = a;
+    vs[i] = a / 448.0f;
+}
+
+__global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, int H, int64_t Npad,
+                                                        const float *__restrict__ km, const float *__restrict__ vs,
+                                                        int8_t *__restrict__ kc, float *__restrict__ ks,
+                                                        uint8_t *__restrict__ vc) {
+    __shared__ float red[1][4];
+    __shared__ uint32_t tile[kD][kTile / 4];
+    const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * H + h;
+    float xk[4][8];
+    load_k_smoothed(k, b, h, tb, N, km, bh, xk);
+    float m[1] = {k_local_max(xk)};
+    block_maxes(m, red);
+    const float sk = m[0] / 127.0f;
+    store_int8_codes(xk, sk, sk, tb, bh, Npad, kc);
+    if (threadIdx.x == 0) ks[bh * (Npad / kKBlock) + tb] = sk;
+    v_tile_codes(v, b, h, tb, N, bh, Npad, vs, vc, tile);
 }
 
 // ------------------------------------------------------------ launchers
@@ -278,6 +442,26 @@ hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs
                        nchunk, B, amax, vs);
     hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)(Npad / kTile), H, B), dim3(256), 0, stream, v, N, H, Npad,
                        vs, vc);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, int8_t *qc, float *qs, int8_t *kc,
+                               float *ks, float *km, uint8_t *vc, float *vs, void *workspace, hipStream_t stream) {
+    const int nchunk = (N + kKBlock - 1) / kKBlock;
+    const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
+    const int64_t total = (int64_t)B * H * kD;
+    double *wsk = static_cast<double *>(workspace);
+    float *wsv = reinterpret_cast<float *>(wsk + (int64_t)nchunk * total);
+    float *amax = wsv + (int64_t)nchunk * total;
+    // passes 1 and 3 run over every 64-token block of the padded code buffers
+    // (blocks past N write zero codes and scales); the partials exist for the
+    // nchunk blocks that hold tokens
+    hipLaunchKernelGGL(qkv_pass1_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, q, k, v, N, H, Npad,
+                       nchunk, qc, qs, wsk, wsv);
+    hipLaunchKernelGGL(qkv_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, wsk, wsv, N,
+                       H, nchunk, B, km, amax, vs);
+    hipLaunchKernelGGL(qkv_pass3_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, k, v, N, H, Npad,
+                       km, vs, kc, ks, vc);
     return hipGetLastError();
 }
 

@@ -61,12 +61,15 @@ def lib() -> ctypes.CDLL:
         L.sage_npad.argtypes, L.sage_npad.restype = [i], ctypes.c_int64
         L.sage_qk_workspace_bytes.argtypes, L.sage_qk_workspace_bytes.restype = [i, i, i, i], sz
         L.sage_v_workspace_bytes.argtypes, L.sage_v_workspace_bytes.restype = [i, i, i, i], sz
+        L.sage_qkv_workspace_bytes.argtypes, L.sage_qkv_workspace_bytes.restype = [i, i, i, i], sz
+        L.sage_quantize_qkv.argtypes = [pin, pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_qk.argtypes = [pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_v.argtypes = [pin, i, i, i, i, vp, vp, vp, sz, vp]
         L.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_bf16.argtypes = [pin, pin, pin, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, pin, i, i, i, i, f, pout, vp]
-        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_attn_fwd", "sage_attn_fwd_bf16", "sage_attn_fwd_int8qk"):
+        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_quantize_qkv", "sage_attn_fwd", "sage_attn_fwd_bf16",
+                   "sage_attn_fwd_int8qk"):
             getattr(L, fn).restype = i
         L.sage_status_str.argtypes, L.sage_status_str.restype = [i], ctypes.c_char_p
         _lib = L
@@ -141,6 +144,21 @@ def sage_quantize_v(v, v_codes, v_scale, workspace, stream=None) -> None:
     _check(st, "sage_quantize_v")
 
 
+def sage_qkv_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
+    return lib().sage_qkv_workspace_bytes(B, N, H, D)
+
+
+def sage_quantize_qkv(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
+                      stream=None) -> None:
+    B, N, H, D = _shape(q)
+    qi, ki, vi = bf16_in(q), bf16_in(k), bf16_in(v)
+    st = lib().sage_quantize_qkv(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D, _ptr(q_codes),
+                                 _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(v_codes),
+                                 _ptr(v_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream))
+    _check(st, "sage_quantize_qkv")
+
+
 def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, out, sm_scale=None, stream=None) -> None:
     B, N, H, D = _shape(out)
     if sm_scale is None:
@@ -188,12 +206,20 @@ class Buffers:
         self.v_scale = torch.empty(B, H, D, dtype=torch.float32, device=dev)
         self.ws_qk = torch.empty(max(1, sage_qk_workspace_bytes(B, N, H, D) // 8), dtype=torch.float64, device=dev)
         self.ws_v = torch.empty(max(1, sage_v_workspace_bytes(B, N, H, D) // 4), dtype=torch.float32, device=dev)
+        self.ws_qkv = torch.empty(max(1, sage_qkv_workspace_bytes(B, N, H, D) // 8), dtype=torch.float64,
+                                  device=dev)
 
 
 def quantize(q, k, v, buf: Buffers, stream=None) -> None:
     """qk_quantize (with K smoothing) then v_quantize into `buf`."""
     sage_quantize_qk(q, k, buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.k_mean, buf.ws_qk, stream)
     sage_quantize_v(v, buf.v_codes, buf.v_scale, buf.ws_v, stream)
+
+
+def quantize_qkv(q, k, v, buf: Buffers, stream=None) -> None:
+    """The same codes and scales as quantize(), from the single three-pass call."""
+    sage_quantize_qkv(q, k, v, buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.k_mean, buf.v_codes,
+                      buf.v_scale, buf.ws_qkv, stream)
 
 
 def forward(q, k, v, out, buf: Buffers, sm_scale=None, stream=None) -> None:

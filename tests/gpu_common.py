@@ -38,10 +38,19 @@ def gpu_case(case: inputs.Case) -> inputs.Case:
     return case.to("cuda")
 
 
-def run_quant(gcase: inputs.Case):
-    """Quantise on the GPU; return numpy copies of every output buffer."""
+def run_quant(gcase: inputs.Case, fused: bool = False):
+    """Quantise on the GPU (quantize_qk + quantize_v, or the single quantize_qkv
+    call); return the buffers.  Code buffers start filled with 0x5A so that a
+    missed write cannot pass as a zero."""
     buf = sage.Buffers(gcase.B, gcase.N, gcase.H)
-    sage.quantize(gcase.q, gcase.k, gcase.v, buf)
+    for t in (buf.q_codes, buf.k_codes, buf.v_codes):
+        t.view(torch.uint8).fill_(0x5A)
+    for t in (buf.q_scale, buf.k_scale, buf.k_mean, buf.v_scale):
+        t.fill_(float("nan"))
+    if fused:
+        sage.quantize_qkv(gcase.q, gcase.k, gcase.v, buf)
+    else:
+        sage.quantize(gcase.q, gcase.k, gcase.v, buf)
     torch.cuda.synchronize()
     return buf
 

@@ -43,6 +43,7 @@ def test_status_strings_and_sizes():
     assert sage.sage_qk_workspace_bytes(1, 37810, 56, 128) == 591 * 56 * 128 * 8
     assert sage.sage_v_workspace_bytes(1, 37810, 56, 128) == (148 + 1) * 56 * 128 * 4
     assert sage.sage_qk_workspace_bytes(1, 10, 2, 64) == 0
+    assert sage.sage_qkv_workspace_bytes(1, 37810, 56, 128) == 591 * 56 * 128 * 12 + 56 * 128 * 4
 
 
 def view(data=A, sb=N * 3 * H * D, sn=3 * H * D, sh=D):
@@ -138,3 +139,18 @@ def test_attn_fwd_int8qk_validation():
     assert call(v=sage.BF16In(A, N * 3 * H * D, 64, D)) == STRIDE    # V token rows overlap
     assert call(o=out(sh=0)) == STRIDE
     assert call(sm=float("nan")) == VALUE
+
+
+def test_quantize_qkv_validation():
+    L = sage.lib()
+    wsb = sage.sage_qkv_workspace_bytes(B, N, H, D)
+    call = lambda q=None, ptrs=(A,) * 7, ws=A, w=wsb, Dv=D: L.sage_quantize_qkv(
+        ctypes.byref(q or view()), ctypes.byref(view(A + 2 * H * D)), ctypes.byref(view(A + 4 * H * D)), B, N, H, Dv,
+        *ptrs, ws, w, None)
+    assert call(ptrs=(A, A, A, A, A, None, A)) == NULL
+    assert call(ws=None) == NULL
+    assert call(Dv=96) == SHAPE
+    assert call(ptrs=(A, A, A, A, A, A + 8, A)) == ALIGN
+    assert call(ws=A + 4) == ALIGN
+    assert call(q=view(sn=-8)) == STRIDE
+    assert call(w=wsb - 8) == WORKSPACE

@@ -11,9 +11,9 @@ from tests import gpu_common as G
 pytestmark = pytest.mark.gpu
 
 
-def _check_bitexact(case: inputs.Case, ref: G.OracleRef):
+def _check_bitexact(case: inputs.Case, ref: G.OracleRef, fused: bool = False):
     B, N, H = case.B, case.N, case.H
-    buf = G.run_quant(G.gpu_case(case))
+    buf = G.run_quant(G.gpu_case(case), fused)
     npad = sage.sage_npad(N)
     nq, nk = -(-N // 32), -(-N // 64)
     km = buf.k_mean.cpu().numpy()
@@ -39,18 +39,20 @@ def test_kappa_matches_binding():
     assert sorted(G.kappa()) == list(range(64))
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["qk+v", "qkv"])
 @pytest.mark.parametrize("name", ["tiny", "mid", "block24", "stress"])
-def test_quantizers_bitexact_workloads(name):
-    print("quantizer parity:", name, flush=True)
+def test_quantizers_bitexact_workloads(name, fused):
+    print("quantizer parity:", name, "fused" if fused else "", flush=True)
     ref = G.config_ref(name)
-    _check_bitexact(ref.case, ref)
+    _check_bitexact(ref.case, ref, fused)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["qk+v", "qkv"])
 @pytest.mark.parametrize("N", [1, 31, 32, 33, 63, 64, 65, 127, 129, 255, 257, 4095])
-def test_quantizers_bitexact_ragged(N):
-    print("quantizer parity ragged N =", N, flush=True)
+def test_quantizers_bitexact_ragged(N, fused):
+    print("quantizer parity ragged N =", N, "fused" if fused else "", flush=True)
     case = inputs.packed_case(2, N, 3, seed=N, stress=(N % 2 == 1))
-    _check_bitexact(case, G.OracleRef(case))
+    _check_bitexact(case, G.OracleRef(case), fused)
 
 
 def test_quantizers_hnd_and_packed_layouts_agree():
