@@ -67,6 +67,12 @@ def _load():
         lib.sage_oracle_attn_exact.argtypes = ([_p, _i64, _i64, _i64] * 3 +
                                                [_int, _int, _int, _int, _dbl, _p, _int, _p])
         lib.sage_oracle_attn_method.argtypes = ([_p] * 6 + [_int] * 7 + [_dbl, _dbl, _int, _p, _int, _p])
+        lib.sage_oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.sage_oracle_e2m1_decode.restype = ctypes.c_double
+        lib.sage_oracle_e2m1_encode.argtypes = [ctypes.c_double]
+        lib.sage_oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.sage_oracle_mx_quantize.argtypes = [_p, _i64, _int, _int, _p, _p]
+        lib.sage_oracle_mx_quantize.restype = None
         lib.sage_oracle_attn_int8qk.argtypes = ([_p] * 4 + [_p, _i64, _i64, _i64] + [_int] * 7 +
                                                 [_dbl, _int, _p, _int, _p])
         for f in ("sage_oracle_kmean", "sage_oracle_quant_q", "sage_oracle_quant_k", "sage_oracle_quant_v",
@@ -237,6 +243,45 @@ def attn_int8qk(qc, qs, kc, ks, v: View, sm_scale: float, rows=None, qblk: int =
     _load().sage_oracle_attn_int8qk(pqc, pqs, pkc, pks, *v.args(), B, N, H, D, qblk, kblk, ptile, sm_scale,
                                     int(round_p), rows.ctypes.data, R, out.ctypes.data)
     return out
+
+
+MX_E4M3, MX_E2M1 = 0, 1
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([_load().sage_oracle_e2m1_decode(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e2m1_encode(x) -> np.ndarray:
+    x = np.asarray(x, dtype=np.float64)
+    return np.array([_load().sage_oracle_e2m1_encode(float(v)) for v in x.ravel()], np.uint8).reshape(x.shape)
+
+
+def mx_quantize(x, fmt: int):
+    """OCP MX blocks of 32 along the last axis of x (values taken exactly as fp64).
+    Returns (codes, scales): codes [..., C] (E4M3) or [..., C/2] (E2M1 pairs),
+    scales [..., C/32] E8M0 bytes."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    C = x.shape[-1]
+    assert C % 32 == 0
+    rows = x.size // C
+    codes = np.zeros(x.shape[:-1] + (C if fmt == MX_E4M3 else C // 2,), np.uint8)
+    scales = np.zeros(x.shape[:-1] + (C // 32,), np.uint8)
+    _load().sage_oracle_mx_quantize(x.ctypes.data, rows, C, fmt, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def mx_dequantize(codes, scales, fmt: int) -> np.ndarray:
+    """Values of MX blocks: element * 2^(scale - 127)."""
+    codes = np.asarray(codes, np.uint8)
+    if fmt == MX_E4M3:
+        el = e4m3_decode(codes).reshape(codes.shape)
+    else:
+        table = e2m1_decode(np.arange(16))
+        el = np.stack([table[codes & 0xF], table[codes >> 4]], axis=-1).reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
+    sc = np.ldexp(1.0, np.asarray(scales, np.int64) - 127)
+    return el * np.repeat(sc, 32, axis=-1)
 
 
 def rel_l2(a, ref) -> float:

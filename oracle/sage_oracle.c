@@ -113,6 +113,86 @@ void sage_oracle_e4m3_decode_array(const uint8_t *c, i64 n, double *out)
         out[i] = sage_oracle_e4m3_decode(c[i]);
 }
 
+/* ---------------------------------- OCP microscaling (MX) formats ---- */
+/* E2M1 (the FP4 element type of MXFP4, OCP Microscaling Formats v1.0): a sign
+ * bit, a 2-bit exponent (bias 1) and a 1-bit mantissa.  Codes 0..7 are the
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (0 and 0.5 subnormal); bit 3 is the
+ * sign.  There is no infinity or NaN. */
+double sage_oracle_e2m1_decode(uint8_t c)
+{
+    static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double m = mag[c & 7];
+    return (c & 8) ? -m : m;
+}
+
+/* Nearest E2M1 magnitude, ties to the even code, saturating at 6; the sign of
+ * zero is kept.  (Written as a search over the eight magnitudes.) */
+uint8_t sage_oracle_e2m1_encode(double x)
+{
+    uint8_t sign = signbit(x) ? 8 : 0;
+    double a = fabs(x);
+    int best = 0;
+    double bestd = INFINITY;
+    for (int c = 0; c < 8; c++) {
+        double d = fabs(a - sage_oracle_e2m1_decode((uint8_t)c));
+        if (d < bestd || (d == bestd && (c & 1) == 0)) {
+            best = c;
+            bestd = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* MX quantisation (OCP Microscaling Formats v1.0, conversion to an MX block):
+ * rows of `cols` values (cols a multiple of 32) in blocks of 32 consecutive
+ * values.  Per block: amax = max |x_i|; shared exponent X = floor(log2 amax) -
+ * emax_elem, with emax_elem the exponent of the element type's largest normal
+ * (8 for E4M3, 2 for E2M1), clamped to [-127, 127]; X = -127 when amax = 0
+ * (reading: the spec leaves the all-zero block's scale open; the smallest is
+ * taken).  The scale is the E8M0 byte X + 127; each element is the element
+ * type's round-to-nearest-even, saturating encoding of x_i / 2^X.
+ * fmt 0: MXFP8 with E4M3 elements, one byte each.  fmt 1: MXFP4 with E2M1
+ * elements, two per byte, the even element in the low nibble.
+ * codes: rows * cols (fmt 0) or rows * cols / 2 (fmt 1) bytes; scales:
+ * rows * cols / 32 bytes. */
+void sage_oracle_mx_quantize(const double *x, i64 rows, int cols, int fmt, uint8_t *codes, uint8_t *scales)
+{
+    int emax = fmt == 0 ? 8 : 2;
+    int nb = cols / 32;
+    for (i64 r = 0; r < rows; r++)
+        for (int blk = 0; blk < nb; blk++) {
+            const double *v = x + r * cols + blk * 32;
+            double amax = 0.0;
+            for (int i = 0; i < 32; i++)
+                if (fabs(v[i]) > amax)
+                    amax = fabs(v[i]);
+            int X = -127;
+            if (amax > 0.0) {
+                int e2;
+                frexp(amax, &e2); /* amax = f * 2^e2, f in [0.5, 1): floor(log2 amax) = e2 - 1 */
+                X = (e2 - 1) - emax;
+                if (X < -127)
+                    X = -127;
+                if (X > 127)
+                    X = 127;
+            }
+            scales[r * nb + blk] = (uint8_t)(X + 127);
+            for (int i = 0; i < 32; i++) {
+                double y = ldexp(v[i], -X); /* exact: a power-of-two scaling */
+                if (fmt == 0) {
+                    codes[r * cols + blk * 32 + i] = sage_oracle_e4m3_encode((float)y);
+                } else {
+                    uint8_t c = sage_oracle_e2m1_encode(y);
+                    i64 byte = (r * cols + blk * 32 + i) / 2;
+                    if (i % 2 == 0)
+                        codes[byte] = c;
+                    else
+                        codes[byte] |= (uint8_t)(c << 4);
+                }
+            }
+        }
+}
+
 /* ------------------------------------------------------------- K mean ---- */
 /* K smoothing statistic: the token mean of K per (batch, head, channel).
  * Reading: summed in fp64, first over `chunk` consecutive tokens in ascending
