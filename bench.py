@@ -15,6 +15,9 @@ Prints ONE JSON line.  Besides the contract keys it carries:
   stages        -- per-stage ms and the quantisers' achieved HBM bandwidth.
   bf16_path     -- the unquantised BF16-MFMA path on the same inputs.
   int8qk_path   -- INT8 Q K^T with the bf16 V unquantised (BF16 P.V) on the same inputs.
+  mx_path       -- the attention with its output written as OCP MX blocks (E4M3 and
+                   E2M1) by the fused epilogue, against attention + the standalone
+                   MX quantiser (sage_mx_quantize) on the bf16 output.
   cpu_baseline  -- the CPU oracle (quantisers in full + step-by-step quantised
                    attention on sampled rows, extrapolated), on the host cores.
 
@@ -250,6 +253,31 @@ def main():
     stream.synchronize()
     int8qk_ms = [e[0].elapsed_time(e[1]) for e in eq]
 
+    # MX output: fused epilogue vs the standalone quantiser over the bf16 output
+    mx = {}
+    for fmt, name in ((sage.MX_E4M3, "e4m3"), (sage.MX_E2M1, "e2m1")):
+        codes, scales = sage.mx_out(B, N, H, fmt, device=dev)
+        ef = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.bf16_calls)]
+        sage.sage_attn_fwd_mx(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, fmt,
+                              codes, scales, sm, stream)
+        for e in ef:
+            e[0].record(stream)
+            sage.sage_attn_fwd_mx(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, fmt,
+                                  codes, scales, sm, stream)
+            e[1].record(stream)
+            sage.sage_mx_quantize(out, fmt, codes, scales, stream)
+            e[2].record(stream)
+        stream.synchronize()
+        fused = [e[0].elapsed_time(e[1]) for e in ef]
+        alone = [e[1].elapsed_time(e[2]) for e in ef]
+        mx_bytes = B * N * H * D * 2 + codes.numel() + scales.numel()
+        mx[name] = {"attn_fwd_mx_ms": stats_ms(fused),
+                    "tflops": flops / (statistics.fmean(fused) * 1e-3) / 1e12,
+                    "mx_quantize_ms": stats_ms(alone),
+                    "mx_quantize_GBps": mx_bytes / (statistics.fmean(alone) * 1e-3) / 1e9,
+                    "unfused_ms": attn_mean + statistics.fmean(alone)}
+        del codes, scales
+
     line = {
         "metric": METRIC,
         "value": value,
@@ -287,6 +315,7 @@ def main():
                         "tflops": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12,
                         "frac_of_peak": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12 / PEAK_INT8QK_TFLOPS,
                         "peak_note": "half the ops at the INT8 peak, half at the BF16 peak: 1/(0.5/5000 + 0.5/2500)"},
+        "mx_path": mx,
         "pages_context": {"gb10_attention_forward_p50_ms": 238.995, "gb10_total_excluding_layout_ms": 258.613,
                           "note": "NVIDIA GB10 on real activations; context only"},
         "input_generation_s": gen_s,

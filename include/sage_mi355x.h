@@ -54,6 +54,8 @@ extern "C" {
 #define SAGE_K_BLOCK 64   /* tokens per K scale (= keys per softmax tile) */
 #define SAGE_P_TILE 64    /* keys per online-softmax step; P is rounded per tile */
 #define SAGE_N_ALIGN 256  /* code buffers hold round_up(N, 256) tokens */
+#define SAGE_MX_E4M3 0    /* MXFP8: E4M3 elements, one byte each */
+#define SAGE_MX_E2M1 1    /* MXFP4: E2M1 elements, two per byte */
 
 typedef enum {
     SAGE_OK = 0,
@@ -63,7 +65,7 @@ typedef enum {
     SAGE_ERR_ALIGN = 4,     /* a pointer or stride breaks 16-byte alignment */
     SAGE_ERR_WORKSPACE = 5, /* workspace too small */
     SAGE_ERR_HIP = 6,       /* the HIP runtime reported an error */
-    SAGE_ERR_VALUE = 7      /* sm_scale is not finite and positive */
+    SAGE_ERR_VALUE = 7      /* sm_scale not finite and positive, or an unknown format */
 } sage_status;
 
 /* A [B, N, H, D] bf16 view: element (b, n, h, d) is at
@@ -191,6 +193,36 @@ int sage_attn_fwd_bf16(const sage_bf16_in *q, const sage_bf16_in *k, const sage_
 int sage_attn_fwd_int8qk(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes,
                          const float *k_scale, const sage_bf16_in *v, int B, int N, int H, int D,
                          float sm_scale, const sage_bf16_out *out, void *stream);
+
+/* OCP microscaling (MX) output for the projection after attention: the profile
+ * page's next_targets lists a fused low-precision projection epilogue (the
+ * pages' projections run in NVFP4, sage2_block_share_estimates.nvfp4_projections);
+ * MI355X's native block-scaled formats are OCP MX, which its MFMAs consume
+ * directly.  Blocks are 32 consecutive channels of the token-major [B, N, H*D]
+ * row (32 | D, so a block lies in one head).  Per block (OCP Microscaling
+ * Formats v1.0): amax = max |x_i|; X = floor(log2 amax) - emax (8 for E4M3, 2 for
+ * E2M1), clamped to [-127, 127], and -127 when amax is 0; scale byte = X + 127
+ * (E8M0); element i = the round-to-nearest-even, saturating E4M3 (max 448) or
+ * E2M1 (max 6) encoding of x_i / 2^X, sign of zero kept.
+ *   codes: [B, N, H*D] bytes (SAGE_MX_E4M3) or [B, N, H*D/2] (SAGE_MX_E2M1,
+ *     element 2i in the low nibble of byte i), token-major, contiguous;
+ *   scales: [B, N, H*D/32] E8M0 bytes.
+ * Codes and scales are bit-exactly defined by the input values.
+ *
+ * sage_mx_quantize: the MX blocks of a bf16 [B, N, H, D] view (16-byte aligned,
+ * strides multiples of 8).  codes 4-byte aligned.  fmt not one of the two
+ * formats gives SAGE_ERR_VALUE. */
+int sage_mx_quantize(const sage_bf16_in *x, int B, int N, int H, int D, int fmt, uint8_t *codes,
+                     uint8_t *scales, void *stream);
+
+/* sage_attn_fwd with the output written as MX blocks instead of bf16: the
+ * blocks of exactly the bf16 values sage_attn_fwd would write (so the result
+ * equals sage_mx_quantize of that output, byte for byte).  Arguments as
+ * sage_attn_fwd; codes/scales as sage_mx_quantize; rows >= N are not written. */
+int sage_attn_fwd_mx(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes,
+                     const float *k_scale, const uint8_t *v_codes, const float *v_scale,
+                     int B, int N, int H, int D, float sm_scale, int fmt, uint8_t *codes,
+                     uint8_t *scales, void *stream);
 
 /* A static, human-readable name for a sage_status value. */
 const char *sage_status_str(int status);

@@ -15,6 +15,11 @@ hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, int8
                                float *ks, float *km, uint8_t *vc, float *vs, void *workspace, hipStream_t stream);
 hipError_t launch_attn_fwd(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
                            const float *vs, int B, int N, int H, float sm_scale, OutView out, hipStream_t stream);
+hipError_t launch_attn_fwd_mx(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
+                              const float *vs, int B, int N, int H, float sm_scale, int fmt, uint8_t *codes,
+                              uint8_t *scales, hipStream_t stream);
+hipError_t launch_mx_quantize(View x, int B, int N, int H, int fmt, uint8_t *codes, uint8_t *scales,
+                              hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(View q, View k, View v, int B, int N, int H, float sm_scale, OutView out,
                                 hipStream_t stream);
 hipError_t launch_attn_fwd_int8qk(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, View v,
@@ -206,6 +211,34 @@ int sage_attn_fwd_int8qk(const int8_t *q_codes, const float *q_scale, const int8
                                                    to_out(out), static_cast<hipStream_t>(stream)));
 }
 
+int sage_mx_quantize(const sage_bf16_in *x, int B, int N, int H, int D, int fmt, uint8_t *codes, uint8_t *scales,
+                     void *stream) {
+    int st;
+    if ((st = check_in(x))) return st;
+    if (!codes || !scales) return SAGE_ERR_NULL;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if (!aligned(codes, 16)) return SAGE_ERR_ALIGN;
+    if (fmt != SAGE_MX_E4M3 && fmt != SAGE_MX_E2M1) return SAGE_ERR_VALUE;
+    return hip_status(sage::launch_mx_quantize(to_view(x), B, N, H, fmt, codes, scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int sage_attn_fwd_mx(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes, const float *k_scale,
+                     const uint8_t *v_codes, const float *v_scale, int B, int N, int H, int D, float sm_scale, int fmt,
+                     uint8_t *codes, uint8_t *scales, void *stream) {
+    int st;
+    if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !codes || !scales)
+        return SAGE_ERR_NULL;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(v_scale, 4) || !aligned(codes, 4))
+        return SAGE_ERR_ALIGN;
+    if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f)) return SAGE_ERR_VALUE;
+    if (fmt != SAGE_MX_E4M3 && fmt != SAGE_MX_E2M1) return SAGE_ERR_VALUE;
+    return hip_status(sage::launch_attn_fwd_mx(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, B, N, H,
+                                               sm_scale, fmt, codes, scales, static_cast<hipStream_t>(stream)));
+}
+
 const char *sage_status_str(int status) {
     switch (status) {
         case SAGE_OK: return "ok";
@@ -215,7 +248,7 @@ const char *sage_status_str(int status) {
         case SAGE_ERR_ALIGN: return "misaligned pointer or stride";
         case SAGE_ERR_WORKSPACE: return "workspace too small";
         case SAGE_ERR_HIP: return "HIP runtime error";
-        case SAGE_ERR_VALUE: return "invalid sm_scale";
+        case SAGE_ERR_VALUE: return "invalid value (sm_scale or format)";
         default: return "unknown status";
     }
 }

@@ -201,10 +201,14 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
 // are staged two steps ahead of the softmax and V tiles one behind: step t
 // reads K(t+1), V(t-1) from LDS and writes K(t+2), V(t) (loaded from HBM at the
 // start of the step) into the buffers of K(t), V(t-2).
+// OUTF: -1 writes the bf16 output through `out`; kMxE4M3 / kMxE2M1 write the MX
+// blocks of those bf16 values to mx_codes / mx_scales instead.
+template <int OUTF>
 __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
     const int8_t *__restrict__ qc, const float *__restrict__ qs, const int8_t *__restrict__ kc,
     const float *__restrict__ ks, const uint8_t *__restrict__ vc, const float *__restrict__ vs, int N,
-    int H, int64_t Npad, float c_base, OutView out, int nqwg) {
+    int H, int64_t Npad, float c_base, OutView out, uint8_t *__restrict__ mx_codes,
+    uint8_t *__restrict__ mx_scales, int nqwg) {
     // four separate LDS objects, always selected at compile time, so the
     // compiler can tell the buffers being read from the ones being filled
     __shared__ v4i lk0[kChunks], lk1[kChunks], lv0[kChunks], lv1[kChunks];
@@ -303,21 +307,62 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
     const float ltot = pair_sum(lsum);
     const float inv = 1.0f / ltot;
     const int n = q0 + ql;
-    if (n < N) {
-        const float *svp = vs + bh * kD;
-        uint16_t *orow = out.data + (int64_t)b * out.sb + (int64_t)n * out.sn + (int64_t)h * out.sh;
+    const float *svp = vs + bh * kD;
+    if (OUTF < 0) {
+        if (n < N) {
+            uint16_t *orow = out.data + (int64_t)b * out.sb + (int64_t)n * out.sn + (int64_t)h * out.sh;
 #pragma unroll
-        for (int db = 0; db < 4; db++)
+            for (int db = 0; db < 4; db++)
 #pragma unroll
-            for (int g = 0; g < 4; g++) {
-                const int d0 = 32 * db + 8 * g + 4 * hl;   // registers 4g..4g+3: channels d0..d0+3
-                const float sv[4] = {svp[d0], svp[d0 + 1], svp[d0 + 2], svp[d0 + 3]};
-                uint32_t lo = f32_to_bf16(o[db][4 * g] * sv[0] * inv) |
-                              (f32_to_bf16(o[db][4 * g + 1] * sv[1] * inv) << 16);
-                uint32_t hi = f32_to_bf16(o[db][4 * g + 2] * sv[2] * inv) |
-                              (f32_to_bf16(o[db][4 * g + 3] * sv[3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(lo, hi);
+                for (int g = 0; g < 4; g++) {
+                    const int d0 = 32 * db + 8 * g + 4 * hl;   // registers 4g..4g+3: channels d0..d0+3
+                    const float sv[4] = {svp[d0], svp[d0 + 1], svp[d0 + 2], svp[d0 + 3]};
+                    uint32_t lo = f32_to_bf16(o[db][4 * g] * sv[0] * inv) |
+                                  (f32_to_bf16(o[db][4 * g + 1] * sv[1] * inv) << 16);
+                    uint32_t hi = f32_to_bf16(o[db][4 * g + 2] * sv[2] * inv) |
+                                  (f32_to_bf16(o[db][4 * g + 3] * sv[3] * inv) << 16);
+                    *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(lo, hi);
+                }
+        }
+    } else {
+        // MX blocks: channel block db (32 channels) of this query is split over the
+        // lane pair (hl = 0, 1), 16 values each; the block maximum needs both.
+        const int64_t row = ((int64_t)b * N + n) * H + h;   // token-major (b, n, h) row of 4 blocks
+#pragma unroll
+        for (int db = 0; db < 4; db++) {
+            float x[16];
+            float amax = 0.0f;
+#pragma unroll
+            for (int g = 0; g < 4; g++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int d = 32 * db + 8 * g + 4 * hl + i;
+                    x[4 * g + i] = bf16_to_f32(f32_to_bf16(o[db][4 * g + i] * svp[d] * inv));
+                    amax = fmaxf(amax, fabsf(x[4 * g + i]));
+                }
+            amax = pair_max(amax);
+            const int X = mx_shared_exp(amax, OUTF == kMxE4M3 ? 8 : 2);
+            const float sc = pow2f(-X);
+            if (n < N) {
+                const int64_t blk = row * (kD / kMxBlock) + db;
+                if (hl == 0) mx_scales[blk] = (uint8_t)(X + 127);
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int e0 = 8 * g + 4 * hl;   // element index of x[4g] within the block
+                    if (OUTF == kMxE4M3) {
+                        const uint32_t wd = e4m3_encode(x[4 * g] * sc) | (e4m3_encode(x[4 * g + 1] * sc) << 8) |
+                                            (e4m3_encode(x[4 * g + 2] * sc) << 16) |
+                                            (e4m3_encode(x[4 * g + 3] * sc) << 24);
+                        *reinterpret_cast<uint32_t *>(mx_codes + blk * kMxBlock + e0) = wd;
+                    } else {
+                        const uint32_t hw = e2m1_encode(x[4 * g] * sc) | (e2m1_encode(x[4 * g + 1] * sc) << 4) |
+                                            (e2m1_encode(x[4 * g + 2] * sc) << 8) |
+                                            (e2m1_encode(x[4 * g + 3] * sc) << 12);
+                        *reinterpret_cast<uint16_t *>(mx_codes + blk * (kMxBlock / 2) + e0 / 2) = (uint16_t)hw;
+                    }
+                }
             }
+        }
     }
 }
 
@@ -328,8 +373,24 @@ hipError_t launch_attn_fwd(const int8_t *qc, const float *qs, const int8_t *kc, 
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     const int nqwg = (N + kQWg - 1) / kQWg;
     const int64_t blocks = (int64_t)nqwg * H * B;
-    hipLaunchKernelGGL(attn_i8f8_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc, ks, vc, vs,
-                       N, H, Npad, sm_scale * kLog2E, out, nqwg);
+    hipLaunchKernelGGL(attn_i8f8_kernel<-1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc, ks, vc,
+                       vs, N, H, Npad, sm_scale * kLog2E, out, nullptr, nullptr, nqwg);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_mx(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
+                              const float *vs, int B, int N, int H, float sm_scale, int fmt, uint8_t *codes,
+                              uint8_t *scales, hipStream_t stream) {
+    const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
+    const int nqwg = (N + kQWg - 1) / kQWg;
+    const int64_t blocks = (int64_t)nqwg * H * B;
+    const OutView none{nullptr, 0, 0, 0};
+    if (fmt == kMxE4M3)
+        hipLaunchKernelGGL(attn_i8f8_kernel<kMxE4M3>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc,
+                           ks, vc, vs, N, H, Npad, sm_scale * kLog2E, none, codes, scales, nqwg);
+    else
+        hipLaunchKernelGGL(attn_i8f8_kernel<kMxE2M1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc,
+                           ks, vc, vs, N, H, Npad, sm_scale * kLog2E, none, codes, scales, nqwg);
     return hipGetLastError();
 }
 

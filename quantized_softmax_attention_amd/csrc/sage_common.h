@@ -70,6 +70,31 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
     return sign | code;
 }
 
+// ---- OCP microscaling (MX, Microscaling Formats v1.0) blocks of 32 values
+// Shared exponent of a block whose largest magnitude is amax (finite, >= 0):
+// floor(log2 amax) - emax_elem clamped to [-127, 127], and -127 when amax is 0
+// or below the fp32 normal range (the clamp would give -127 there anyway).
+__device__ __forceinline__ int mx_shared_exp(float amax, int emax_elem) {
+    const uint32_t ebits = __float_as_uint(amax) >> 23;
+    if (ebits == 0) return -127;
+    return max(-127, min(127, (int)ebits - 127 - emax_elem));
+}
+
+// 2^n for n in [-126, 127].
+__device__ __forceinline__ float pow2f(int n) { return __uint_as_float((uint32_t)(n + 127) << 23); }
+
+// E2M1 (FP4): nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, ties to the even code,
+// saturating at 6; bit 3 carries the sign (also of zero).
+__device__ __forceinline__ uint32_t e2m1_encode(float y) {
+    const float a = fabsf(y);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+constexpr int kMxE4M3 = SAGE_MX_E4M3, kMxE2M1 = SAGE_MX_E2M1;
+constexpr int kMxBlock = 32;
+
 // Workgroup index remap so that the workgroups one XCD receives (hardware
 // dispatch is round-robin over the 8 XCDs) form one contiguous range of the
 // logical grid: XCD x works on logical ids [x*n/8, (x+1)*n/8).  Identity when

@@ -36,7 +36,7 @@ import numpy as np
 import torch
 
 # stream ids: each random component has its own stream
-_S_Q, _S_K, _S_V, _S_OFFSET, _S_OUTLIER, _S_T_NUM, _S_T_DEN, _S_ROWS, _S_X = range(1, 10)
+_S_Q, _S_K, _S_V, _S_OFFSET, _S_OUTLIER, _S_T_NUM, _S_T_DEN, _S_ROWS, _S_X, _S_MX_EXP, _S_MX_KIND = range(1, 12)
 _CHUNK_ROWS = 512
 
 
@@ -193,6 +193,27 @@ def config(name: str, seed: int = 0) -> Case:
     if layout == "hnd":
         return hnd_case(B, N, H, D, seed=seed, name=name)
     return packed_case(B, N, H, D, seed=seed, stress=stress, name=name)
+
+
+def mx_tensor(B: int, N: int, H: int, D: int = 128, seed: int = 0) -> torch.Tensor:
+    """A contiguous bf16 [B, N, H, D] tensor for microscaling tests: N(0, 1) values,
+    each 32-channel block scaled by 2^e with e uniform in [-60, 60], and blocks
+    picked at random (about 1 in 16 of each kind) set to zero, to -0.0, to one
+    nonzero value among zeros, or to values near the bottom of the bf16 range
+    (2^-140 .. 2^-120, subnormals included)."""
+    x = normal_f32((B, N, H, D), seed, _S_X)
+    nb = B * N * H * (D // 32)
+    g = _gen(seed, _S_MX_EXP)
+    e = torch.randint(-60, 61, (nb, 1), generator=g).float()
+    kind = torch.randint(0, 16, (nb,), generator=_gen(seed, _S_MX_KIND))
+    blocks = x.reshape(nb, 32) * torch.exp2(e)
+    blocks[kind == 0] = 0.0
+    blocks[kind == 1] = -0.0
+    lone = kind == 2
+    blocks[lone, 1:] = 0.0
+    tiny = kind == 3
+    blocks[tiny] = x.reshape(nb, 32)[tiny] * torch.exp2(torch.randint(-140, -119, (int(tiny.sum()), 1), generator=g).float())
+    return blocks.reshape(B, N, H, D).to(torch.bfloat16)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -68,8 +68,10 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_bf16.argtypes = [pin, pin, pin, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, pin, i, i, i, i, f, pout, vp]
+        L.sage_mx_quantize.argtypes = [pin, i, i, i, i, i, vp, vp, vp]
+        L.sage_attn_fwd_mx.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, vp]
         for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_quantize_qkv", "sage_attn_fwd", "sage_attn_fwd_bf16",
-                   "sage_attn_fwd_int8qk"):
+                   "sage_attn_fwd_int8qk", "sage_mx_quantize", "sage_attn_fwd_mx"):
             getattr(L, fn).restype = i
         L.sage_status_str.argtypes, L.sage_status_str.restype = [i], ctypes.c_char_p
         _lib = L
@@ -187,6 +189,43 @@ def sage_attn_fwd_int8qk(q_codes, q_scale, k_codes, k_scale, v, out, sm_scale=No
     st = lib().sage_attn_fwd_int8qk(_ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), ctypes.byref(vi),
                                     B, N, H, D, float(sm_scale), ctypes.byref(o), _stream(stream))
     _check(st, "sage_attn_fwd_int8qk")
+
+
+MX_E4M3, MX_E2M1 = 0, 1
+
+
+def mx_out(B: int, N: int, H: int, fmt: int, device="cuda", D: int = HEAD_DIM):
+    """Token-major MX output buffers: codes [B, N, H*D] (E4M3) or [B, N, H*D/2]
+    (E2M1 pairs) and E8M0 scales [B, N, H*D/32]."""
+    per = H * D if fmt == MX_E4M3 else H * D // 2
+    dev = torch.device(device)
+    return (torch.empty(B, N, per, dtype=torch.uint8, device=dev),
+            torch.empty(B, N, H * D // 32, dtype=torch.uint8, device=dev))
+
+
+def _mx_shape(codes, scales, fmt):
+    B, N, per = codes.shape
+    H = scales.shape[2] * 32 // HEAD_DIM
+    assert per == (H * HEAD_DIM if fmt == MX_E4M3 else H * HEAD_DIM // 2)
+    return B, N, H
+
+
+def sage_mx_quantize(x, fmt: int, codes, scales, stream=None) -> None:
+    B, N, H, D = _shape(x)
+    xi = bf16_in(x)
+    st = lib().sage_mx_quantize(ctypes.byref(xi), B, N, H, D, int(fmt), _ptr(codes), _ptr(scales), _stream(stream))
+    _check(st, "sage_mx_quantize")
+
+
+def sage_attn_fwd_mx(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, fmt: int, codes, scales, sm_scale=None,
+                     stream=None) -> None:
+    B, N, H = _mx_shape(codes, scales, fmt)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    st = lib().sage_attn_fwd_mx(_ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes),
+                                _ptr(v_scale), B, N, H, HEAD_DIM, float(sm_scale), int(fmt), _ptr(codes),
+                                _ptr(scales), _stream(stream))
+    _check(st, "sage_attn_fwd_mx")
 
 
 class Buffers:

@@ -154,3 +154,29 @@ def test_quantize_qkv_validation():
     assert call(ws=A + 4) == ALIGN
     assert call(q=view(sn=-8)) == STRIDE
     assert call(w=wsb - 8) == WORKSPACE
+
+
+def test_mx_quantize_validation():
+    L = sage.lib()
+    call = lambda x=None, c=A, s=A, fmt=0, Dv=D: L.sage_mx_quantize(ctypes.byref(x or view()), B, N, H, Dv, fmt, c, s,
+                                                                   None)
+    assert call(c=None) == NULL and call(s=None) == NULL
+    assert call(x=view(data=None)) == NULL
+    assert call(Dv=64) == SHAPE
+    assert call(c=A + 8) == ALIGN
+    assert call(x=view(data=A + 2)) == ALIGN
+    assert call(x=view(sh=-D)) == STRIDE
+    assert call(fmt=2) == VALUE and call(fmt=-1) == VALUE
+
+
+def test_attn_fwd_mx_validation():
+    L = sage.lib()
+    call = lambda ptrs=(A,) * 6, c=A, s=A, sm=0.088, fmt=1, Nv=N: L.sage_attn_fwd_mx(*ptrs, B, Nv, H, D, sm, fmt, c, s,
+                                                                                     None)
+    assert call(ptrs=(A, A, A, A, None, A)) == NULL
+    assert call(c=None) == NULL and call(s=None) == NULL
+    assert call(Nv=0) == SHAPE
+    assert call(c=A + 2) == ALIGN
+    assert call(ptrs=(A, A, A + 4, A, A, A)) == ALIGN
+    assert call(sm=float("inf")) == VALUE
+    assert call(fmt=7) == VALUE

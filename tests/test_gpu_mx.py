@@ -1,0 +1,128 @@
+"""OCP microscaling (MX) output on the GPU through the C ABI.
+
+* sage_mx_quantize: byte-exact against the oracle's MX quantiser (the rule is
+  deterministic: shared exponent from the block maximum, nearest-even element
+  rounding), on blocks spanning the bf16 range, zero and -0.0 blocks, lone
+  values and subnormals, contiguous and strided inputs.
+* sage_attn_fwd_mx: byte-exact against sage_mx_quantize applied to the bf16
+  output of sage_attn_fwd on the same codes (the fused epilogue must round to
+  bf16 first and then quantise exactly as the standalone pass does), and
+  against the oracle: the dequantised MX output is as close to the method's
+  exact output as the oracle's own MX quantisation of it (plus the attention
+  kernel's 1e-3-level deviation), with scales equal up to one binade where the
+  block maximum sits at a power of two."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_softmax_attention_amd import inputs, sage
+from tests import gpu_common as G
+
+pytestmark = pytest.mark.gpu
+
+FMTS = [sage.MX_E4M3, sage.MX_E2M1]
+
+
+def _mx_oracle(x: torch.Tensor, fmt):
+    B, N, H, D = x.shape
+    return oracle.mx_quantize(x.cpu().double().numpy().reshape(B, N, H * D), fmt)
+
+
+def _fill(*ts):
+    for t in ts:
+        t.fill_(0x5A)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 300, 3), (2, 129, 56)])
+def test_mx_quantize_bitexact(fmt, shape):
+    B, N, H = shape
+    print("mx_quantize", fmt, shape, flush=True)
+    x = inputs.mx_tensor(B, N, H, seed=11 + N)
+    codes, scales = sage.mx_out(B, N, H, fmt)
+    _fill(codes, scales)
+    sage.sage_mx_quantize(x.cuda(), fmt, codes, scales)
+    torch.cuda.synchronize()
+    wc, ws = _mx_oracle(x, fmt)
+    assert np.array_equal(scales.cpu().numpy(), ws)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mx_quantize_strided_view(fmt):
+    # Q/K/V-style column range of a packed [B, N, 3*H*D] buffer
+    B, N, H = 2, 77, 4
+    base = inputs.mx_tensor(B, N, 3 * H, seed=5)
+    view = base.cuda().reshape(B, N, 3 * H * 128)[:, :, H * 128:2 * H * 128].unflatten(2, (H, 128))
+    codes, scales = sage.mx_out(B, N, H, fmt)
+    _fill(codes, scales)
+    sage.sage_mx_quantize(view, fmt, codes, scales)
+    torch.cuda.synchronize()
+    wc, ws = _mx_oracle(base[:, :, H:2 * H], fmt)
+    assert np.array_equal(scales.cpu().numpy(), ws)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+
+
+def _fused_vs_standalone(gcase, fmt, buf=None):
+    out, buf = G.run_attn(gcase, buf)
+    B, N, H = gcase.B, gcase.N, gcase.H
+    c1, s1 = sage.mx_out(B, N, H, fmt)
+    c2, s2 = sage.mx_out(B, N, H, fmt)
+    _fill(c1, s1, c2, s2)
+    sage.sage_mx_quantize(out, fmt, c1, s1)
+    sage.sage_attn_fwd_mx(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, fmt, c2, s2,
+                          G.SM)
+    torch.cuda.synchronize()
+    return out, (c1, s1), (c2, s2), buf
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("N", [1, 33, 64, 300, 1000])
+def test_attn_mx_equals_mx_of_bf16_output(fmt, N):
+    print("attn_mx vs mx(attn) N =", N, "fmt", fmt, flush=True)
+    case = inputs.packed_case(2, N, 3, seed=700 + N, stress=(N % 2 == 1))
+    _, (c1, s1), (c2, s2), _ = _fused_vs_standalone(G.gpu_case(case), fmt)
+    assert torch.equal(s1, s2)
+    assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_attn_mx_block24_equals_mx_of_bf16_output(fmt):
+    print("attn_mx block24 fmt", fmt, flush=True)
+    _, (c1, s1), (c2, s2), _ = _fused_vs_standalone(G.gpu_case(inputs.config("block24")), fmt)
+    assert torch.equal(s1, s2)
+    assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_attn_mx_vs_oracle(fmt):
+    print("attn_mx vs oracle fmt", fmt, flush=True)
+    ref = G.config_ref("tiny")
+    case = ref.case
+    rows = inputs.sample_rows(case.B, case.H, case.N, count=case.N)
+    meth = G.bf16_round(ref.method(rows))                  # [B, H, N, D], rows = all tokens in order
+    want = np.ascontiguousarray(meth.transpose(0, 2, 1, 3)).reshape(case.B, case.N, case.H * case.D)
+    wc, ws = oracle.mx_quantize(want, fmt)
+    _, _, (c2, s2), _ = _fused_vs_standalone(G.gpu_case(case), fmt)
+    gc, gs = c2.cpu().numpy(), s2.cpu().numpy()
+    d = gs.astype(int) - ws.astype(int)
+    assert np.abs(d).max() <= 1 and (d != 0).mean() <= 0.02
+    deq_gpu = oracle.mx_dequantize(gc, gs, fmt)
+    deq_orc = oracle.mx_dequantize(wc, ws, fmt)
+    e_gpu, e_orc = G.rel_l2(deq_gpu, want), G.rel_l2(deq_orc, want)
+    print("fmt %d: rel-L2 of MX output vs method output: GPU %.4e, oracle %.4e" % (fmt, e_gpu, e_orc), flush=True)
+    assert e_gpu <= 1.05 * e_orc + 2e-3
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_attn_mx_rows_beyond_n_untouched(fmt):
+    case = G.gpu_case(inputs.packed_case(1, 70, 2, seed=4))
+    buf = G.run_quant(case)
+    c, s = sage.mx_out(1, 128, 2, fmt)
+    _fill(c, s)
+    sage.sage_attn_fwd_mx(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, fmt,
+                          c[:, :70], s[:, :70], G.SM)
+    torch.cuda.synchronize()
+    assert torch.all(c[:, 70:] == 0x5A) and torch.all(s[:, 70:] == 0x5A)
+    assert not torch.all(s[:, :70] == 0x5A)
