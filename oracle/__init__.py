@@ -73,6 +73,11 @@ def _load():
         lib.sage_oracle_e2m1_encode.restype = ctypes.c_uint8
         lib.sage_oracle_mx_quantize.argtypes = [_p, _i64, _int, _int, _p, _p]
         lib.sage_oracle_mx_quantize.restype = None
+        lib.sage_oracle_norm_rope.argtypes = [_p, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p,
+                                              ctypes.c_float, _int, _p]
+        lib.sage_oracle_norm_rope.restype = None
+        lib.sage_oracle_norm_rope_f64.argtypes = [_p, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p, _dbl, _p]
+        lib.sage_oracle_norm_rope_f64.restype = None
         lib.sage_oracle_attn_int8qk.argtypes = ([_p] * 4 + [_p, _i64, _i64, _i64] + [_int] * 7 +
                                                 [_dbl, _int, _p, _int, _p])
         for f in ("sage_oracle_kmean", "sage_oracle_quant_q", "sage_oracle_quant_k", "sage_oracle_quant_v",
@@ -282,6 +287,29 @@ def mx_dequantize(codes, scales, fmt: int) -> np.ndarray:
         el = np.stack([table[codes & 0xF], table[codes >> 4]], axis=-1).reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
     sc = np.ldexp(1.0, np.asarray(scales, np.int64) - 127)
     return el * np.repeat(sc, 32, axis=-1)
+
+
+def norm_rope(x: View, gamma, rope, eps: float, chunk: int = 8) -> np.ndarray:
+    """RMSNorm over each head row's D channels (weight gamma[D]) then RoPE on
+    channel pairs (2i, 2i+1) with rope[n, i] = (cos, sin), in the fixed fp32
+    order written out in sage_oracle.c; bf16 result bits, [B, N, H, D] uint16."""
+    g, pg = _c(np.asarray(gamma, np.float32).reshape(-1), np.float32)
+    r, pr = _c(np.asarray(rope, np.float32), np.float32)
+    assert g.size == x.D and r.shape == (x.N, x.D // 2, 2)
+    out = np.empty((x.B, x.N, x.H, x.D), np.uint16)
+    _load().sage_oracle_norm_rope(*x.args(), x.B, x.N, x.H, x.D, pg, pr, float(np.float32(eps)), chunk,
+                                  out.ctypes.data)
+    return out
+
+
+def norm_rope_f64(x: View, gamma, rope, eps: float) -> np.ndarray:
+    """The same transform in fp64, unrounded: [B, N, H, D] float64."""
+    g, pg = _c(np.asarray(gamma, np.float32).reshape(-1), np.float32)
+    r, pr = _c(np.asarray(rope, np.float32), np.float32)
+    assert g.size == x.D and r.shape == (x.N, x.D // 2, 2)
+    out = np.empty((x.B, x.N, x.H, x.D), np.float64)
+    _load().sage_oracle_norm_rope_f64(*x.args(), x.B, x.N, x.H, x.D, pg, pr, float(eps), out.ctypes.data)
+    return out
 
 
 def rel_l2(a, ref) -> float:

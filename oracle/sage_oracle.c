@@ -463,17 +463,19 @@ void sage_oracle_attn_method(const int8_t *qc, const float *qs, const int8_t *kc
 /* ------------------------------ INT8 Q K^T with an unquantised P.V ---- */
 /* bf16 of an fp32 value: round to nearest, ties to even (finite values), as the
  * bfloat16 format is defined (the upper 16 bits of an IEEE binary32). */
-static double bf16_rne(float x)
+static uint16_t bf16_rne_bits(float x)
 {
     uint32_t u;
     memcpy(&u, &x, sizeof u);
     uint32_t lower = u & 0xFFFFu, upper = u >> 16;
     if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
         upper += 1u;
-    u = upper << 16;
-    float r;
-    memcpy(&r, &u, sizeof r);
-    return (double)r;
+    return (uint16_t)upper;
+}
+
+static double bf16_rne(float x)
+{
+    return (double)bf16_to_f32(bf16_rne_bits(x));
 }
 
 /* The "sol_int8_qk" precision split of the profile page
@@ -541,6 +543,97 @@ void sage_oracle_attn_int8qk(const int8_t *qc, const float *qs, const int8_t *kc
         free(s);
         free(acc);
     }
+}
+
+/* ------------------------------------------- RMSNorm + RoPE of Q and K ---- */
+/* [strided] dataflow.qk_transform: before quantisation, Q and K go through
+ * RMSNorm and rotary position embedding, in place on their strided views;
+ * [profile] representative_block_24_p50_milliseconds.sage2.rms_rope prices the
+ * step.  The pages print no formula.  Reading (the plainest one for a per-head
+ * [B, N, H, D] view):
+ *   - RMSNorm over the D channels of one (b, n, h) row with a learned weight
+ *     gamma[D] shared by all heads: r = 1 / sqrt(mean_d x_d^2 + eps),
+ *     y_d = x_d * r * gamma_d;
+ *   - RoPE on adjacent channel pairs (2i, 2i+1) with a per-token angle table
+ *     rope[n][i] = (cos, sin) shared by batches and heads:
+ *     (a, b) -> (a cos - b sin, a sin + b cos);
+ *   - the result stored as bf16, rounded once (nearest even).
+ *
+ * The bf16 result decides INT8 codes downstream, so the fp32 arithmetic is
+ * written out with a fixed order (the order the GPU kernel uses):
+ *   ss  = the squares of `chunk` consecutive channels summed left to right, the
+ *         D/chunk partial sums then combined as a pairwise tree in channel order
+ *         ((s0+s1)+(s2+s3))+...;
+ *   r   = 1 / sqrtf(ss / D + eps)          (IEEE sqrt and division)
+ *   n_d = (x_d * r) * gamma_d
+ *   y   = (n_2i * c - n_2i+1 * s,  n_2i * s + n_2i+1 * c)
+ * every operation rounded to fp32, none fused.  D/chunk must be a power of 2. */
+static float sum_squares_f32(const float *x, int D, int chunk)
+{
+    float part[64];
+    int m = D / chunk;
+    for (int c = 0; c < m; c++) {
+        float a = 0.0f;
+        for (int j = 0; j < chunk; j++) {
+            float sq = x[c * chunk + j] * x[c * chunk + j];
+            a = (j == 0) ? sq : a + sq;
+        }
+        part[c] = a;
+    }
+    for (int w = 1; w < m; w *= 2)          /* pairwise: (0,1), (2,3), ... then ((0,1),(2,3)), ... */
+        for (int c = 0; c < m; c += 2 * w)
+            part[c] = part[c] + part[c + w];
+    return part[0];
+}
+
+void sage_oracle_norm_rope(const uint16_t *x, i64 sb, i64 sn, i64 sh, int B, int N, int H, int D,
+                           const float *gamma, const float *rope, float eps, int chunk, uint16_t *out)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int n = 0; n < N; n++)
+            for (int h = 0; h < H; h++) {
+                float xr[512], nr[512];
+                for (int d = 0; d < D; d++) xr[d] = load_bf16(x, sb, sn, sh, b, n, h, d);
+                float ss = sum_squares_f32(xr, D, chunk);
+                float r = 1.0f / sqrtf(ss / (float)D + eps);
+                for (int d = 0; d < D; d++) nr[d] = (xr[d] * r) * gamma[d];
+                uint16_t *o = out + (((i64)b * N + n) * H + h) * D;
+                for (int i = 0; i < D / 2; i++) {
+                    float c = rope[((i64)n * (D / 2) + i) * 2], s = rope[((i64)n * (D / 2) + i) * 2 + 1];
+                    float a = nr[2 * i], e = nr[2 * i + 1];
+                    float y0 = a * c - e * s;
+                    float y1 = a * s + e * c;
+                    o[2 * i] = bf16_rne_bits(y0);
+                    o[2 * i + 1] = bf16_rne_bits(y1);
+                }
+            }
+}
+
+/* The same transform in fp64 without any intermediate rounding and without the
+ * bf16 rounding (any summation order: exact enough to bound the fp32 one). */
+void sage_oracle_norm_rope_f64(const uint16_t *x, i64 sb, i64 sn, i64 sh, int B, int N, int H, int D,
+                               const float *gamma, const float *rope, double eps, double *out)
+{
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < B; b++)
+        for (int n = 0; n < N; n++)
+            for (int h = 0; h < H; h++) {
+                double ss = 0.0;
+                for (int d = 0; d < D; d++) {
+                    double v = load_bf16(x, sb, sn, sh, b, n, h, d);
+                    ss += v * v;
+                }
+                double r = 1.0 / sqrt(ss / D + eps);
+                double *o = out + (((i64)b * N + n) * H + h) * D;
+                for (int i = 0; i < D / 2; i++) {
+                    double c = rope[((i64)n * (D / 2) + i) * 2], s = rope[((i64)n * (D / 2) + i) * 2 + 1];
+                    double a = load_bf16(x, sb, sn, sh, b, n, h, 2 * i) * r * gamma[2 * i];
+                    double e = load_bf16(x, sb, sn, sh, b, n, h, 2 * i + 1) * r * gamma[2 * i + 1];
+                    o[2 * i] = a * c - e * s;
+                    o[2 * i + 1] = a * s + e * c;
+                }
+            }
 }
 
 /* Threads the OpenMP loops above use (reported beside oracle timings). */

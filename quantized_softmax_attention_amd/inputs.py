@@ -36,7 +36,8 @@ import numpy as np
 import torch
 
 # stream ids: each random component has its own stream
-_S_Q, _S_K, _S_V, _S_OFFSET, _S_OUTLIER, _S_T_NUM, _S_T_DEN, _S_ROWS, _S_X, _S_MX_EXP, _S_MX_KIND = range(1, 12)
+(_S_Q, _S_K, _S_V, _S_OFFSET, _S_OUTLIER, _S_T_NUM, _S_T_DEN, _S_ROWS, _S_X, _S_MX_EXP, _S_MX_KIND,
+ _S_GAMMA) = range(1, 13)
 _CHUNK_ROWS = 512
 
 
@@ -214,6 +215,48 @@ def mx_tensor(B: int, N: int, H: int, D: int = 128, seed: int = 0) -> torch.Tens
     tiny = kind == 3
     blocks[tiny] = x.reshape(nb, 32)[tiny] * torch.exp2(torch.randint(-140, -119, (int(tiny.sum()), 1), generator=g).float())
     return blocks.reshape(B, N, H, D).to(torch.bfloat16)
+
+
+@dataclass
+class NormRope:
+    """Parameters of the RMSNorm + RoPE applied to Q and K before quantisation."""
+    gamma_q: torch.Tensor     # [D] fp32 (bf16-representable values)
+    gamma_k: torch.Tensor     # [D] fp32
+    rope: torch.Tensor        # [N, D/2, 2] fp32: (cos, sin) of each token's angle per channel pair
+    eps: float
+
+    def to(self, device) -> "NormRope":
+        return NormRope(self.gamma_q.to(device), self.gamma_k.to(device), self.rope.to(device), self.eps)
+
+
+def video_rope_table(N: int, D: int = 128, width: int = 42, height: int = 24, theta: float = 10000.0) -> torch.Tensor:
+    """Rotary angles of a video token grid: token n sits at frame n // (w*h), row
+    and column of a width x height latent frame (1344x768 with 32-pixel cells);
+    the D/2 channel pairs split into frame / row / column bands of 16 / 24 / 24
+    pairs, band pair j at frequency theta^(-j / band).  cos and sin are computed
+    in fp64 and rounded to fp32.  [N, D/2, 2]"""
+    pairs = D // 2
+    bands = [pairs // 4, (pairs - pairs // 4) // 2]
+    bands.append(pairs - bands[0] - bands[1])
+    n = np.arange(N, dtype=np.int64)
+    pos = [n // (width * height), (n // width) % height, n % width]
+    ang = np.empty((N, pairs), np.float64)
+    p0 = 0
+    for band, ps in zip(bands, pos):
+        freq = theta ** (-np.arange(band, dtype=np.float64) / band)
+        ang[:, p0:p0 + band] = ps[:, None].astype(np.float64) * freq[None, :]
+        p0 += band
+    tab = np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)
+    return torch.from_numpy(tab)
+
+
+def norm_rope_params(N: int, D: int = 128, seed: int = 0, eps: float = 1e-6) -> NormRope:
+    """Seeded RMSNorm weights (uniform in [0.5, 1.5), rounded to bf16 values) for
+    Q and K, the video rotary table and eps."""
+    g = _gen(seed, _S_GAMMA)
+    gq = (0.5 + torch.rand(D, generator=g)).to(torch.bfloat16).float()
+    gk = (0.5 + torch.rand(D, generator=g)).to(torch.bfloat16).float()
+    return NormRope(gq, gk, video_rope_table(N, D), eps)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
