@@ -15,6 +15,9 @@ Prints ONE JSON line.  Besides the contract keys it carries:
   stages        -- per-stage ms and the quantisers' achieved HBM bandwidth.
   bf16_path     -- the unquantised BF16-MFMA path on the same inputs.
   int8qk_path   -- INT8 Q K^T with the bf16 V unquantised (BF16 P.V) on the same inputs.
+  rope_path     -- RMSNorm + RoPE of Q and K before quantisation: in place
+                   (sage_qk_norm_rope) then sage_quantize_qkv, against the fused
+                   sage_quantize_qkv_rope (same codes, Q and K never written).
   mx_path       -- the attention with its output written as OCP MX blocks (E4M3 and
                    E2M1) by the fused epilogue, against attention + the standalone
                    MX quantiser (sage_mx_quantize) on the bf16 output.
@@ -61,6 +64,18 @@ def quant_bytes(b=B, n=N, h=H, d=D) -> dict:
         # V read for the channel maxima, V read again for the codes, fp8 codes written
         "v_quantize": 2 * e + 2 * e + codes,
     }
+
+
+def rope_bytes(b=B, n=N, h=H, d=D) -> dict:
+    """Algorithmic HBM bytes of the RMSNorm + RoPE step: in place, Q and K read
+    and written once plus the rotary table (fp32 cos/sin per token and channel
+    pair); fused into the quantiser, its bytes are the quantiser's plus the
+    table once per pass that reads Q or K (two)."""
+    e = b * n * h * d
+    table = n * d * 4
+    qb = quant_bytes(b, n, h, d)
+    return {"norm_rope": 4 * 2 * e + table,
+            "qkv_rope": qb["qk_quantize"] + qb["v_quantize"] + 2 * table}
 
 
 def attn_bytes(b=B, n=N, h=H, d=D) -> int:
@@ -253,6 +268,35 @@ def main():
     stream.synchronize()
     int8qk_ms = [e[0].elapsed_time(e[1]) for e in eq]
 
+    # RMSNorm + RoPE of Q and K: in place then quantise, vs fused into the quantiser
+    nr = inputs.norm_rope_params(N).to(dev)
+    pk = g.packed.clone()                 # the in-place transform works on a copy
+    HD = H * D
+    pq, pk_k = (pk[:, :, i * HD:(i + 1) * HD].unflatten(2, (H, D)) for i in range(2))
+    rbuf = sage.Buffers(B, N, H, device=dev)
+    er = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.bf16_calls)]
+    sage.quantize_qkv_rope(g.q, g.k, g.v, nr, rbuf, stream)
+    for e in er:
+        e[0].record(stream)
+        sage.sage_qk_norm_rope(pq, pk_k, nr.gamma_q, nr.gamma_k, nr.rope, nr.eps, stream)
+        e[1].record(stream)
+        sage.quantize_qkv(pq, pk_k, g.v, rbuf, stream)
+        e[2].record(stream)
+        sage.quantize_qkv_rope(g.q, g.k, g.v, nr, rbuf, stream)
+        e[3].record(stream)
+    stream.synchronize()
+    nr_ms = [e[0].elapsed_time(e[1]) for e in er]
+    unf_ms = [e[0].elapsed_time(e[2]) for e in er]
+    fused_ms = [e[2].elapsed_time(e[3]) for e in er]
+    rb = rope_bytes()
+    rope = {"norm_rope_ms": stats_ms(nr_ms),
+            "norm_rope_GBps": rb["norm_rope"] / (statistics.fmean(nr_ms) * 1e-3) / 1e9,
+            "unfused_norm_rope_plus_qkv_ms": stats_ms(unf_ms),
+            "qkv_rope_fused_ms": stats_ms(fused_ms),
+            "qkv_rope_fused_GBps": rb["qkv_rope"] / (statistics.fmean(fused_ms) * 1e-3) / 1e9,
+            "pages_context": {"gb10_block24_rms_rope_p50_ms": 12.535, "note": "NVIDIA GB10, whole rms_rope component"}}
+    del pk, rbuf
+
     # MX output: fused epilogue vs the standalone quantiser over the bf16 output
     mx = {}
     for fmt, name in ((sage.MX_E4M3, "e4m3"), (sage.MX_E2M1, "e2m1")):
@@ -315,6 +359,7 @@ def main():
                         "tflops": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12,
                         "frac_of_peak": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12 / PEAK_INT8QK_TFLOPS,
                         "peak_note": "half the ops at the INT8 peak, half at the BF16 peak: 1/(0.5/5000 + 0.5/2500)"},
+        "rope_path": rope,
         "mx_path": mx,
         "pages_context": {"gb10_attention_forward_p50_ms": 238.995, "gb10_total_excluding_layout_ms": 258.613,
                           "note": "NVIDIA GB10 on real activations; context only"},

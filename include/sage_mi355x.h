@@ -65,7 +65,7 @@ typedef enum {
     SAGE_ERR_ALIGN = 4,     /* a pointer or stride breaks 16-byte alignment */
     SAGE_ERR_WORKSPACE = 5, /* workspace too small */
     SAGE_ERR_HIP = 6,       /* the HIP runtime reported an error */
-    SAGE_ERR_VALUE = 7      /* sm_scale not finite and positive, or an unknown format */
+    SAGE_ERR_VALUE = 7      /* sm_scale or eps not finite and positive, or an unknown format */
 } sage_status;
 
 /* A [B, N, H, D] bf16 view: element (b, n, h, d) is at
@@ -148,6 +148,37 @@ int sage_quantize_qkv(const sage_bf16_in *q, const sage_bf16_in *k, const sage_b
                       int D, int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale,
                       float *k_mean, uint8_t *v_codes, float *v_scale, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* The step before quantisation: RMSNorm and rotary position embedding of Q and K
+ * in place on their strided views (strided page, dataflow.qk_transform; profile
+ * page, representative_block_24_p50_milliseconds.sage2.rms_rope).  For every
+ * (b, n, h) row x of D channels:
+ *   r   = 1 / sqrt(ss / D + eps), ss = sum_d x_d^2
+ *   y_d = (x_d * r) * gamma[d]                       (gamma_q for Q, gamma_k for K)
+ *   (y_2i, y_2i+1) <- (y_2i c - y_2i+1 s,  y_2i s + y_2i+1 c),  (c, s) = rope[n][i]
+ *   x <- bf16(y), round to nearest even.
+ * fp32 arithmetic, every product and sum rounded (no fused multiply-add), IEEE
+ * sqrt and division; ss adds the squares of 8 consecutive channels left to right
+ * and combines the 16 partials as a pairwise tree in channel order
+ * ((p0 + p1) + (p2 + p3)) + ...  The result is bit-exactly defined by this.
+ *   q, k: [B, N, H, D] views written in place: 16-byte aligned, strides
+ *     multiples of 8, distinct (b, n, h) rows (else SAGE_ERR_STRIDE); Q and K
+ *     must not share elements (not checked).
+ *   gamma_q, gamma_k: [D] fp32; rope: [N, D/2, 2] fp32 (cos, sin) pairs, the
+ *     same for every batch and head; all 16-byte aligned, device memory.
+ *   eps: finite and > 0 (else SAGE_ERR_VALUE). */
+int sage_qk_norm_rope(const sage_bf16_out *q, const sage_bf16_out *k, int B, int N, int H, int D,
+                      const float *gamma_q, const float *gamma_k, const float *rope, float eps, void *stream);
+
+/* sage_qk_norm_rope fused into sage_quantize_qkv: the codes, scales and k_mean
+ * that sage_qk_norm_rope followed by sage_quantize_qkv produce, bit for bit, with
+ * Q and K read once less and not written (the transformed Q and K are not
+ * materialised; q and k are only read).  Arguments as the two calls. */
+int sage_quantize_qkv_rope(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N, int H,
+                           int D, const float *gamma_q, const float *gamma_k, const float *rope, float eps,
+                           int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale, float *k_mean,
+                           uint8_t *v_codes, float *v_scale, void *workspace, size_t workspace_bytes,
+                           void *stream);
 
 /* attention_forward (profile page, attention_internal_p50_milliseconds.sage2
  * .attention_forward; latency page, the whole artefact): from the buffers the two

@@ -5,14 +5,17 @@
 #include <cstdint>
 
 #include "sage_common.h"
+#include "sage_norm_rope.h"
 
 namespace sage {
 hipError_t launch_quantize_qk(View q, View k, int B, int N, int H, int8_t *qc, float *qs, int8_t *kc,
                               float *ks, float *km, void *workspace, hipStream_t stream);
 hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs, void *workspace,
                              hipStream_t stream);
-hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, int8_t *qc, float *qs, int8_t *kc,
-                               float *ks, float *km, uint8_t *vc, float *vs, void *workspace, hipStream_t stream);
+hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, const NormRope *nr, int8_t *qc, float *qs,
+                               int8_t *kc, float *ks, float *km, uint8_t *vc, float *vs, void *workspace,
+                               hipStream_t stream);
+hipError_t launch_norm_rope(OutView q, OutView k, int B, int N, int H, NormRope nr, hipStream_t stream);
 hipError_t launch_attn_fwd(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
                            const float *vs, int B, int N, int H, float sm_scale, OutView out, hipStream_t stream);
 hipError_t launch_attn_fwd_mx(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
@@ -90,6 +93,26 @@ sage::OutView to_out(const sage_bf16_out *o) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SAGE_OK : SAGE_ERR_HIP; }
 
+// A view transformed in place: rows are read and written whole with 16-byte
+// accesses, so as an input view, plus distinct rows.
+int check_inplace(const sage_bf16_out *v, int B, int N, int H) {
+    if (!v || !v->data) return SAGE_ERR_NULL;
+    if (v->stride_b < 0 || v->stride_n < 0 || v->stride_h < 0) return SAGE_ERR_STRIDE;
+    if (!aligned(v->data, 16)) return SAGE_ERR_ALIGN;
+    if (v->stride_b % 8 || v->stride_n % 8 || v->stride_h % 8) return SAGE_ERR_ALIGN;
+    if (!rows_disjoint(v->stride_b, v->stride_n, v->stride_h, B, N, H)) return SAGE_ERR_STRIDE;
+    return SAGE_OK;
+}
+
+// RMSNorm weights and rotary table: read with 16-byte loads; eps > 0 keeps
+// all-zero rows finite.
+int check_norm_rope(const float *gamma_q, const float *gamma_k, const float *rope, float eps) {
+    if (!gamma_q || !gamma_k || !rope) return SAGE_ERR_NULL;
+    if (!aligned(gamma_q, 16) || !aligned(gamma_k, 16) || !aligned(rope, 16)) return SAGE_ERR_ALIGN;
+    if (!std::isfinite(eps) || !(eps > 0.0f)) return SAGE_ERR_VALUE;
+    return SAGE_OK;
+}
+
 // K and V tiles of a strided view are staged as 64 token rows through 32-bit,
 // row-bounded buffer offsets: token rows may not overlap and a tile must span
 // < 2 GiB.
@@ -163,7 +186,38 @@ int sage_quantize_qkv(const sage_bf16_in *q, const sage_bf16_in *k, const sage_b
         !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4) || !aligned(workspace, 8))
         return SAGE_ERR_ALIGN;
     if (workspace_bytes < sage_qkv_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
-    return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, q_codes, q_scale,
+    return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, nullptr, q_codes,
+                                                q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int sage_qk_norm_rope(const sage_bf16_out *q, const sage_bf16_out *k, int B, int N, int H, int D,
+                      const float *gamma_q, const float *gamma_k, const float *rope, float eps, void *stream) {
+    int st;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if ((st = check_inplace(q, B, N, H)) || (st = check_inplace(k, B, N, H))) return st;
+    if ((st = check_norm_rope(gamma_q, gamma_k, rope, eps))) return st;
+    return hip_status(sage::launch_norm_rope(to_out(q), to_out(k), B, N, H,
+                                             sage::NormRope{gamma_q, gamma_k, rope, eps},
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int sage_quantize_qkv_rope(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N, int H,
+                           int D, const float *gamma_q, const float *gamma_k, const float *rope, float eps,
+                           int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale, float *k_mean,
+                           uint8_t *v_codes, float *v_scale, void *workspace, size_t workspace_bytes, void *stream) {
+    int st;
+    if ((st = check_in(q)) || (st = check_in(k)) || (st = check_in(v))) return st;
+    if (!q_codes || !q_scale || !k_codes || !k_scale || !k_mean || !v_codes || !v_scale || !workspace)
+        return SAGE_ERR_NULL;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if ((st = check_norm_rope(gamma_q, gamma_k, rope, eps))) return st;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4) || !aligned(workspace, 8))
+        return SAGE_ERR_ALIGN;
+    if (workspace_bytes < sage_qkv_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
+    const sage::NormRope nr{gamma_q, gamma_k, rope, eps};
+    return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, &nr, q_codes, q_scale,
                                                 k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
                                                 static_cast<hipStream_t>(stream)));
 }
@@ -248,7 +302,7 @@ const char *sage_status_str(int status) {
         case SAGE_ERR_ALIGN: return "misaligned pointer or stride";
         case SAGE_ERR_WORKSPACE: return "workspace too small";
         case SAGE_ERR_HIP: return "HIP runtime error";
-        case SAGE_ERR_VALUE: return "invalid value (sm_scale or format)";
+        case SAGE_ERR_VALUE: return "invalid value (sm_scale, eps or format)";
         default: return "unknown status";
     }
 }

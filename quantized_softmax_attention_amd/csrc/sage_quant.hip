@@ -10,6 +10,7 @@
 // All kernels here are HBM-bound.  Their results are bit-exact by definition:
 // no FMA contraction, IEEE fp32 division, fixed fp64 summation order.
 #include "sage_common.h"
+#include "sage_norm_rope.h"
 
 #pragma clang fp contract(off)
 
@@ -70,6 +71,87 @@ __device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int j = 0; j < 8; j++) x[j] = bf16_to_f32((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+}
+
+// ------------------------------------------------ RMSNorm + RoPE of Q and K
+// "gb10-sage-strided-nhd-summary-1344x768-124f-seed440420.json",
+// dataflow.qk_transform: Q and K pass through RMSNorm and rotary embedding on
+// their strided views before quantisation.  Per (b, n, h) row of D = 128:
+//   r = 1 / sqrt(sum_d x_d^2 / D + eps),  y_d = (x_d * r) * gamma_d,
+//   channel pairs (2i, 2i+1) turned by the token's angle: (a c - b s, a s + b c),
+// rounded once to bf16.  The 16 threads of a row are 16 consecutive lanes
+// (seg = lane % 16, channels 8*seg..+7).  Each adds the squares of its 8
+// channels left to right; an xor butterfly over the 16 lanes then combines the
+// partials as a pairwise tree in channel order (every lane ends with the same
+// bits: fp32 addition is commutative).  No contraction (see the pragma above):
+// every product and sum is rounded to fp32, so the result is bit-exactly
+// defined.  Must be called by all 16 lanes of the row; n is clamped by the caller
+// to a valid token (rows past N are discarded afterwards).
+__device__ __forceinline__ void norm_rope8(float (&x)[8], const float *__restrict__ gamma,
+                                           const float *__restrict__ rope, int n, float eps) {
+    const int seg = threadIdx.x & 15;
+    float a = x[0] * x[0];
+#pragma unroll
+    for (int j = 1; j < 8; j++) a = a + x[j] * x[j];
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) a = a + __shfl_xor(a, o, 64);
+    const float r = 1.0f / __builtin_sqrtf(a / (float)kD + eps);
+    const float4 g0 = *reinterpret_cast<const float4 *>(gamma + 8 * seg);
+    const float4 g1 = *reinterpret_cast<const float4 *>(gamma + 8 * seg + 4);
+    const float4 *tr = reinterpret_cast<const float4 *>(rope + ((int64_t)n * (kD / 2) + 4 * seg) * 2);
+    const float4 t0 = tr[0], t1 = tr[1];
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    float y[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) y[j] = (x[j] * r) * g[j];
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+        const float c = cs[2 * p], s = cs[2 * p + 1];
+        x[2 * p] = bf16_to_f32(f32_to_bf16(y[2 * p] * c - y[2 * p + 1] * s));
+        x[2 * p + 1] = bf16_to_f32(f32_to_bf16(y[2 * p] * s + y[2 * p + 1] * c));
+    }
+}
+
+// The transformed row of token n (x as loaded; zeros stay zeros for n >= N).
+__device__ __forceinline__ void norm_rope_row(float (&x)[8], const float *__restrict__ gamma, const NormRope &nr,
+                                              int n, int N) {
+    norm_rope8(x, gamma, nr.rope, min(n, N - 1), nr.eps);
+    if (n >= N)
+#pragma unroll
+        for (int j = 0; j < 8; j++) x[j] = 0.0f;
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&x)[8]) {
+    return make_uint4(f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16), f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16),
+                      f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16), f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16));
+}
+
+// In place on the Q and K views: one workgroup per (64-token block, head,
+// batch); thread (row, seg) transforms tokens row + 16 i of both.  All loads
+// are issued before the first store (the views may share a buffer).
+__global__ __launch_bounds__(256) void norm_rope_kernel(OutView q, OutView k, int N, NormRope nr) {
+    const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    uint16_t *qb = q.data + (int64_t)b * q.sb + (int64_t)h * q.sh + seg * 8;
+    uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
+    float xq[4][8], xk[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        load_row8(qb + (int64_t)n * q.sn, n < N, xq[i]);
+        load_row8(kb + (int64_t)n * k.sn, n < N, xk[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        norm_rope_row(xq[i], nr.gamma_q, nr, n, N);
+        norm_rope_row(xk[i], nr.gamma_k, nr, n, N);
+        if (n < N) {
+            *reinterpret_cast<uint4 *>(qb + (int64_t)n * q.sn) = pack_bf16x8(xq[i]);
+            *reinterpret_cast<uint4 *>(kb + (int64_t)n * k.sn) = pack_bf16x8(xk[i]);
+        }
+    }
 }
 
 // ------------------------------------------------------------- INT8 blocks
@@ -141,9 +223,10 @@ __device__ __forceinline__ void store_int8_codes(const float (&x)[4][8], float s
 }
 
 // K of the block, smoothed: x = fp32(k) - k_mean (one fp32 subtraction); zero
-// for tokens >= N.
+// for tokens >= N.  ROPE: k is first replaced by its RMSNorm + RoPE transform.
+template <bool ROPE>
 __device__ __forceinline__ void load_k_smoothed(View k, int b, int h, int tb, int N, const float *__restrict__ km,
-                                                int64_t bh, float (&x)[4][8]) {
+                                                int64_t bh, const NormRope &nr, float (&x)[4][8]) {
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
     const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
     float mean[8];
@@ -153,6 +236,11 @@ __device__ __forceinline__ void load_k_smoothed(View k, int b, int h, int tb, in
     for (int i = 0; i < 4; i++) {
         const int n = tb * 64 + row + 16 * i;
         load_row8(kb + (int64_t)n * k.sn, n < N, x[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        if (ROPE) norm_rope_row(x[i], nr.gamma_k, nr, n, N);
 #pragma unroll
         for (int j = 0; j < 8; j++) x[i][j] = n < N ? x[i][j] - mean[j] : 0.0f;
     }
@@ -179,7 +267,7 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(View q, View k, int N, in
     const int64_t bh = (int64_t)b * H + h;
     float xq[4][8], xk[4][8];
     load_block(q, b, h, tb, N, xq);
-    load_k_smoothed(k, b, h, tb, N, km, bh, xk);
+    load_k_smoothed<false>(k, b, h, tb, N, km, bh, NormRope{}, xk);
     float m[3];
     q_local_max(xq, m[0], m[1]);
     m[2] = k_local_max(xk);
@@ -304,8 +392,11 @@ __global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int6
 //      channel maximum and scale;
 //   3. per (64-token block, head, batch): the K codes and scale (smoothed) and
 //      the block's V codes.
+// ROPE: Q and K are replaced by their RMSNorm + RoPE transform as they are read
+// (the K block is transformed before it is summed and before its codes).
+template <bool ROPE>
 __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, int N, int H, int64_t Npad,
-                                                        int nchunk, int8_t *__restrict__ qc,
+                                                        int nchunk, NormRope nr, int8_t *__restrict__ qc,
                                                         float *__restrict__ qs, double *__restrict__ wsk,
                                                         float *__restrict__ wsv) {
     __shared__ float red[2][4];
@@ -321,9 +412,16 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int n = tb * 64 + row + 16 * i;
-        uint4 rk = make_uint4(0, 0, 0, 0);
-        if (n < N) rk = *reinterpret_cast<const uint4 *>(kb + (int64_t)n * k.sn);
-        kbuf[row + 16 * i][seg] = rk;
+        if (ROPE) {
+            float xk[8];
+            load_row8(kb + (int64_t)n * k.sn, n < N, xk);
+            norm_rope_row(xk, nr.gamma_k, nr, n, N);
+            kbuf[row + 16 * i][seg] = pack_bf16x8(xk);
+        } else {
+            uint4 rk = make_uint4(0, 0, 0, 0);
+            if (n < N) rk = *reinterpret_cast<const uint4 *>(kb + (int64_t)n * k.sn);
+            kbuf[row + 16 * i][seg] = rk;
+        }
         float xv[8];
         load_row8(vb + (int64_t)n * v.sn, n < N, xv);
 #pragma unroll
@@ -333,6 +431,9 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
     for (int j = 0; j < 8; j++) vred[row][seg * 8 + j] = vm[j];
     float xq[4][8];
     load_block(q, b, h, tb, N, xq);
+    if (ROPE)
+#pragma unroll
+        for (int i = 0; i < 4; i++) norm_rope_row(xq[i], nr.gamma_q, nr, tb * 64 + row + 16 * i, N);
     float m[2];
     q_local_max(xq, m[0], m[1]);
     block_maxes(m, red);                             // its barriers also publish kbuf and vred
@@ -396,7 +497,8 @@ __global__ __launch_bounds__(256) void qkv_final_kernel(const double *__restrict
     vs[i] = a / 448.0f;
 }
 
-__global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, int H, int64_t Npad,
+template <bool ROPE>
+__global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, int H, int64_t Npad, NormRope nr,
                                                         const float *__restrict__ km, const float *__restrict__ vs,
                                                         int8_t *__restrict__ kc, float *__restrict__ ks,
                                                         uint8_t *__restrict__ vc) {
@@ -405,7 +507,7 @@ __global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, i
     const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * H + h;
     float xk[4][8];
-    load_k_smoothed(k, b, h, tb, N, km, bh, xk);
+    load_k_smoothed<ROPE>(k, b, h, tb, N, km, bh, nr, xk);
     float m[1] = {k_local_max(xk)};
     block_maxes(m, red);
     const float sk = m[0] / 127.0f;
@@ -445,23 +547,40 @@ hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, int8_t *qc, float *qs, int8_t *kc,
-                               float *ks, float *km, uint8_t *vc, float *vs, void *workspace, hipStream_t stream) {
+// nr == nullptr: Q and K as given; otherwise their RMSNorm + RoPE transform.
+hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, const NormRope *nr, int8_t *qc, float *qs,
+                               int8_t *kc, float *ks, float *km, uint8_t *vc, float *vs, void *workspace,
+                               hipStream_t stream) {
     const int nchunk = (N + kKBlock - 1) / kKBlock;
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     const int64_t total = (int64_t)B * H * kD;
     double *wsk = static_cast<double *>(workspace);
     float *wsv = reinterpret_cast<float *>(wsk + (int64_t)nchunk * total);
     float *amax = wsv + (int64_t)nchunk * total;
+    const NormRope p = nr ? *nr : NormRope{};
+    const dim3 grid((unsigned)(Npad / 64), H, B);
     // passes 1 and 3 run over every 64-token block of the padded code buffers
     // (blocks past N write zero codes and scales); the partials exist for the
     // nchunk blocks that hold tokens
-    hipLaunchKernelGGL(qkv_pass1_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, q, k, v, N, H, Npad,
-                       nchunk, qc, qs, wsk, wsv);
+    if (nr)
+        hipLaunchKernelGGL(qkv_pass1_kernel<true>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
+                           wsk, wsv);
+    else
+        hipLaunchKernelGGL(qkv_pass1_kernel<false>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
+                           wsk, wsv);
     hipLaunchKernelGGL(qkv_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, wsk, wsv, N,
                        H, nchunk, B, km, amax, vs);
-    hipLaunchKernelGGL(qkv_pass3_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, k, v, N, H, Npad,
-                       km, vs, kc, ks, vc);
+    if (nr)
+        hipLaunchKernelGGL(qkv_pass3_kernel<true>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
+                           vc);
+    else
+        hipLaunchKernelGGL(qkv_pass3_kernel<false>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
+                           vc);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_rope(OutView q, OutView k, int B, int N, int H, NormRope nr, hipStream_t stream) {
+    hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)((N + 63) / 64), H, B), dim3(256), 0, stream, q, k, N, nr);
     return hipGetLastError();
 }
 

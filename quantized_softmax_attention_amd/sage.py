@@ -68,10 +68,14 @@ def lib() -> ctypes.CDLL:
         L.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_bf16.argtypes = [pin, pin, pin, i, i, i, i, f, pout, vp]
         L.sage_attn_fwd_int8qk.argtypes = [vp, vp, vp, vp, pin, i, i, i, i, f, pout, vp]
+        L.sage_qk_norm_rope.argtypes = [pout, pout, i, i, i, i, vp, vp, vp, f, vp]
+        L.sage_quantize_qkv_rope.argtypes = [pin, pin, pin, i, i, i, i, vp, vp, vp, f,
+                                             vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sage_mx_quantize.argtypes = [pin, i, i, i, i, i, vp, vp, vp]
         L.sage_attn_fwd_mx.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, vp]
         for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_quantize_qkv", "sage_attn_fwd", "sage_attn_fwd_bf16",
-                   "sage_attn_fwd_int8qk", "sage_mx_quantize", "sage_attn_fwd_mx"):
+                   "sage_attn_fwd_int8qk", "sage_mx_quantize", "sage_attn_fwd_mx", "sage_qk_norm_rope",
+                   "sage_quantize_qkv_rope"):
             getattr(L, fn).restype = i
         L.sage_status_str.argtypes, L.sage_status_str.restype = [i], ctypes.c_char_p
         _lib = L
@@ -159,6 +163,32 @@ def sage_quantize_qkv(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_cod
                                  _ptr(v_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  _stream(stream))
     _check(st, "sage_quantize_qkv")
+
+
+def sage_qk_norm_rope(q, k, gamma_q, gamma_k, rope, eps: float, stream=None) -> None:
+    """RMSNorm + RoPE of the Q and K views, in place."""
+    B, N, H, D = _shape(q)
+    assert tuple(k.shape) == (B, N, H, D) and tuple(rope.shape) == (N, D // 2, 2)
+    assert gamma_q.dtype == gamma_k.dtype == rope.dtype == torch.float32
+    assert gamma_q.is_contiguous() and gamma_k.is_contiguous() and rope.is_contiguous()
+    qo, ko = bf16_out(q), bf16_out(k)
+    st = lib().sage_qk_norm_rope(ctypes.byref(qo), ctypes.byref(ko), B, N, H, D, _ptr(gamma_q), _ptr(gamma_k),
+                                 _ptr(rope), float(eps), _stream(stream))
+    _check(st, "sage_qk_norm_rope")
+
+
+def sage_quantize_qkv_rope(q, k, v, gamma_q, gamma_k, rope, eps: float, q_codes, q_scale, k_codes, k_scale, k_mean,
+                           v_codes, v_scale, workspace, stream=None) -> None:
+    B, N, H, D = _shape(q)
+    assert tuple(rope.shape) == (N, D // 2, 2)
+    assert gamma_q.dtype == gamma_k.dtype == rope.dtype == torch.float32
+    assert gamma_q.is_contiguous() and gamma_k.is_contiguous() and rope.is_contiguous()
+    qi, ki, vi = bf16_in(q), bf16_in(k), bf16_in(v)
+    st = lib().sage_quantize_qkv_rope(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D, _ptr(gamma_q),
+                                      _ptr(gamma_k), _ptr(rope), float(eps), _ptr(q_codes), _ptr(q_scale),
+                                      _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(v_codes), _ptr(v_scale),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sage_quantize_qkv_rope")
 
 
 def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, out, sm_scale=None, stream=None) -> None:
@@ -259,6 +289,13 @@ def quantize_qkv(q, k, v, buf: Buffers, stream=None) -> None:
     """The same codes and scales as quantize(), from the single three-pass call."""
     sage_quantize_qkv(q, k, v, buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.k_mean, buf.v_codes,
                       buf.v_scale, buf.ws_qkv, stream)
+
+
+def quantize_qkv_rope(q, k, v, nr, buf: Buffers, stream=None) -> None:
+    """quantize_qkv of the RMSNorm + RoPE transform of Q and K; nr carries
+    gamma_q, gamma_k, rope (device tensors) and eps."""
+    sage_quantize_qkv_rope(q, k, v, nr.gamma_q, nr.gamma_k, nr.rope, nr.eps, buf.q_codes, buf.q_scale, buf.k_codes,
+                           buf.k_scale, buf.k_mean, buf.v_codes, buf.v_scale, buf.ws_qkv, stream)
 
 
 def forward(q, k, v, out, buf: Buffers, sm_scale=None, stream=None) -> None:

@@ -55,6 +55,31 @@ def run_quant(gcase: inputs.Case, fused: bool = False):
     return buf
 
 
+def check_quant_bitexact(buf, ref: "OracleRef"):
+    """Every quantiser output in buf (GPU) equals the oracle's for ref's case,
+    bit for bit, with zero codes and scales in the padding."""
+    case = ref.case
+    B, N, H = case.B, case.N, case.H
+    npad = sage.sage_npad(N)
+    nq, nk = -(-N // 32), -(-N // 64)
+    km = buf.k_mean.cpu().numpy()
+    assert np.array_equal(km.view(np.uint32), ref.km.view(np.uint32)), "k_mean"
+    qc, qs = buf.q_codes.cpu().numpy(), buf.q_scale.cpu().numpy()
+    kc, ks = buf.k_codes.cpu().numpy(), buf.k_scale.cpu().numpy()
+    (rqc, rqs), (rkc, rks) = ref.qq, ref.kq
+    assert np.array_equal(qc[:, :, :N], rqc), "q_codes"
+    assert np.array_equal(kc[:, :, :N], rkc), "k_codes"
+    assert not qc[:, :, N:].any() and not kc[:, :, N:].any(), "padding codes"
+    assert np.array_equal(qs[:, :, :nq].view(np.uint32), rqs.view(np.uint32)), "q_scale"
+    assert np.array_equal(ks[:, :, :nk].view(np.uint32), rks.view(np.uint32)), "k_scale"
+    assert not qs[:, :, nq:].any() and not ks[:, :, nk:].any(), "padding scales"
+    assert qs.shape == (B, H, npad // 32) and ks.shape == (B, H, npad // 64)
+    vc = unpermute_v(buf.v_codes.cpu().numpy(), N)
+    rvc, rvs = ref.vq
+    assert np.array_equal(buf.v_scale.cpu().numpy().view(np.uint32), rvs.view(np.uint32)), "v_scale"
+    assert np.array_equal(vc, rvc), "v_codes"
+
+
 def run_attn(gcase: inputs.Case, buf=None):
     if buf is None:
         buf = run_quant(gcase)

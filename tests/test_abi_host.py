@@ -180,3 +180,33 @@ def test_attn_fwd_mx_validation():
     assert call(ptrs=(A, A, A + 4, A, A, A)) == ALIGN
     assert call(sm=float("inf")) == VALUE
     assert call(fmt=7) == VALUE
+
+
+def test_qk_norm_rope_validation():
+    L = sage.lib()
+    io = lambda data=A, sn=3 * H * D, sh=D: sage.BF16Out(data, N * 3 * H * D, sn, sh)
+    call = lambda q=None, g=(A, A, A), eps=1e-6, Dv=D: L.sage_qk_norm_rope(
+        ctypes.byref(q or io()), ctypes.byref(io(A + 2 * H * D)), B, N, H, Dv, *g, eps, None)
+    assert call(g=(A, None, A)) == NULL and call(g=(A, A, None)) == NULL
+    assert call(q=io(data=None)) == NULL
+    assert call(Dv=64) == SHAPE
+    assert call(q=io(data=A + 8)) == ALIGN
+    assert call(q=io(sn=3 * H * D + 4)) == ALIGN
+    assert call(g=(A, A, A + 4)) == ALIGN and call(g=(A + 8, A, A)) == ALIGN
+    assert call(q=io(sh=64)) == STRIDE                 # heads overlap
+    assert call(eps=0.0) == VALUE and call(eps=float("nan")) == VALUE and call(eps=-1.0) == VALUE
+
+
+def test_quantize_qkv_rope_validation():
+    L = sage.lib()
+    wsb = sage.sage_qkv_workspace_bytes(B, N, H, D)
+    call = lambda g=(A, A, A), eps=1e-6, ptrs=(A,) * 7, ws=A, w=wsb, Dv=D: L.sage_quantize_qkv_rope(
+        ctypes.byref(view()), ctypes.byref(view(A + 2 * H * D)), ctypes.byref(view(A + 4 * H * D)), B, N, H, Dv,
+        *g, eps, *ptrs, ws, w, None)
+    assert call(g=(None, A, A)) == NULL
+    assert call(ptrs=(A, A, None, A, A, A, A)) == NULL
+    assert call(Dv=256) == SHAPE
+    assert call(g=(A, A, A + 4)) == ALIGN
+    assert call(ptrs=(A + 8, A, A, A, A, A, A)) == ALIGN
+    assert call(eps=float("inf")) == VALUE
+    assert call(w=wsb - 8) == WORKSPACE

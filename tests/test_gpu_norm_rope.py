@@ -1,0 +1,118 @@
+"""RMSNorm + RoPE of Q and K on the GPU through the C ABI.
+
+* sage_qk_norm_rope (in place): the transformed Q and K equal the oracle's
+  fixed-order fp32 evaluation bit for bit, on HND and packed strided views,
+  ragged N and the block-24 workload; nothing outside the two views changes.
+* sage_quantize_qkv_rope (fused): every code, scale and k_mean equals the
+  oracle's quantisers applied to the oracle's transformed Q and K, bit for bit,
+  and equals sage_qk_norm_rope followed by sage_quantize_qkv on the GPU; the
+  inputs are left untouched.  The attention over the fused codes matches the
+  method oracle on the transformed inputs."""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_softmax_attention_amd import inputs, sage
+from tests import gpu_common as G
+from tests.helpers import oracle_view
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits_tensor(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+
+
+def _oracle_transformed(case: inputs.Case, nr: inputs.NormRope) -> inputs.Case:
+    """The case with Q and K replaced by the oracle's transform (contiguous
+    [B, N, H, D]); V as it was."""
+    tq = oracle.norm_rope(oracle_view(case.q), nr.gamma_q.numpy(), nr.rope.numpy(), nr.eps)
+    tk = oracle.norm_rope(oracle_view(case.k), nr.gamma_k.numpy(), nr.rope.numpy(), nr.eps)
+    return inputs.Case(case.name + "+rope", case.B, case.N, case.H, case.D, _bits_tensor(tq), _bits_tensor(tk),
+                       case.v)
+
+
+def _storage_hash(t: torch.Tensor) -> str:
+    return hashlib.sha256(t.cpu().view(torch.int16).numpy().tobytes()).hexdigest()
+
+
+CASES = {
+    "tiny": lambda: inputs.config("tiny"),
+    "packed_ragged": lambda: inputs.packed_case(2, 300, 3, seed=31, stress=True),
+    "one_token": lambda: inputs.packed_case(1, 1, 1, seed=32),
+    "n65": lambda: inputs.packed_case(1, 65, 4, seed=33),
+    "block24": lambda: inputs.config("block24"),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_norm_rope_in_place_bitexact(name):
+    print("norm_rope in place:", name, flush=True)
+    case = CASES[name]()
+    nr = inputs.norm_rope_params(case.N, seed=3)
+    want = _oracle_transformed(case, nr)
+    g = G.gpu_case(case)
+    before_v = _storage_hash(g.v.contiguous())
+    packed_before = None if g.packed is None else g.packed.clone()
+    sage.sage_qk_norm_rope(g.q, g.k, nr.to("cuda").gamma_q, nr.to("cuda").gamma_k, nr.rope.cuda(), nr.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(g.q.cpu().view(torch.int16), want.q.view(torch.int16)), "Q"
+    assert torch.equal(g.k.cpu().view(torch.int16), want.k.view(torch.int16)), "K"
+    assert _storage_hash(g.v.contiguous()) == before_v, "V changed"
+    if packed_before is not None:
+        HD = case.H * case.D
+        assert torch.equal(g.packed[:, :, 2 * HD:], packed_before[:, :, 2 * HD:])
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_quantize_qkv_rope_bitexact_vs_oracle(name):
+    print("quantize_qkv_rope vs oracle:", name, flush=True)
+    case = CASES[name]()
+    nr = inputs.norm_rope_params(case.N, seed=4)
+    ref = G.OracleRef(_oracle_transformed(case, nr))
+    g = G.gpu_case(case)
+    src_before = _storage_hash(g.packed if g.packed is not None else torch.cat([g.q, g.k, g.v]))
+    buf = sage.Buffers(case.B, case.N, case.H)
+    for t in (buf.q_codes, buf.k_codes, buf.v_codes):
+        t.view(torch.uint8).fill_(0x5A)
+    for t in (buf.q_scale, buf.k_scale, buf.k_mean, buf.v_scale):
+        t.fill_(float("nan"))
+    sage.quantize_qkv_rope(g.q, g.k, g.v, nr.to("cuda"), buf)
+    torch.cuda.synchronize()
+    G.check_quant_bitexact(buf, ref)
+    assert _storage_hash(g.packed if g.packed is not None else torch.cat([g.q, g.k, g.v])) == src_before
+
+
+@pytest.mark.parametrize("N", [1, 33, 64, 129, 1000])
+def test_fused_equals_in_place_then_quantize(N):
+    print("fused vs unfused N =", N, flush=True)
+    case = inputs.packed_case(2, N, 3, seed=40 + N, stress=(N % 2 == 1))
+    nr = inputs.norm_rope_params(N, seed=5).to("cuda")
+    a = G.gpu_case(case)
+    fused = sage.Buffers(case.B, N, case.H)
+    sage.quantize_qkv_rope(a.q, a.k, a.v, nr, fused)
+    b = G.gpu_case(case)
+    sage.sage_qk_norm_rope(b.q, b.k, nr.gamma_q, nr.gamma_k, nr.rope, nr.eps)
+    unfused = sage.Buffers(case.B, N, case.H)
+    sage.quantize_qkv(b.q, b.k, b.v, unfused)
+    torch.cuda.synchronize()
+    for f in ("q_codes", "q_scale", "k_codes", "k_scale", "k_mean", "v_codes", "v_scale"):
+        assert torch.equal(getattr(fused, f), getattr(unfused, f)), f
+
+
+def test_attention_over_fused_codes_matches_method():
+    case = inputs.config("tiny")
+    nr = inputs.norm_rope_params(case.N, seed=6)
+    ref = G.OracleRef(_oracle_transformed(case, nr))
+    g = G.gpu_case(case)
+    buf = sage.Buffers(case.B, case.N, case.H)
+    sage.quantize_qkv_rope(g.q, g.k, g.v, nr.to("cuda"), buf)
+    out, _ = G.run_attn(g, buf)
+    rows = inputs.sample_rows(case.B, case.H, case.N, count=case.N)
+    got = G.out_rows(out, rows)
+    e = G.rel_l2(got, G.bf16_round(ref.method(rows)))
+    print("attention after fused norm+rope quantisation: rel-L2 vs method oracle %.3e" % e, flush=True)
+    assert e <= 1e-3

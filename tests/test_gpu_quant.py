@@ -12,26 +12,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _check_bitexact(case: inputs.Case, ref: G.OracleRef, fused: bool = False):
-    B, N, H = case.B, case.N, case.H
-    buf = G.run_quant(G.gpu_case(case), fused)
-    npad = sage.sage_npad(N)
-    nq, nk = -(-N // 32), -(-N // 64)
-    km = buf.k_mean.cpu().numpy()
-    assert np.array_equal(km.view(np.uint32), ref.km.view(np.uint32)), "k_mean"
-    qc, qs = buf.q_codes.cpu().numpy(), buf.q_scale.cpu().numpy()
-    kc, ks = buf.k_codes.cpu().numpy(), buf.k_scale.cpu().numpy()
-    (rqc, rqs), (rkc, rks) = ref.qq, ref.kq
-    assert np.array_equal(qc[:, :, :N], rqc), "q_codes"
-    assert np.array_equal(kc[:, :, :N], rkc), "k_codes"
-    assert not qc[:, :, N:].any() and not kc[:, :, N:].any(), "padding codes"
-    assert np.array_equal(qs[:, :, :nq].view(np.uint32), rqs.view(np.uint32)), "q_scale"
-    assert np.array_equal(ks[:, :, :nk].view(np.uint32), rks.view(np.uint32)), "k_scale"
-    assert not qs[:, :, nq:].any() and not ks[:, :, nk:].any(), "padding scales"
-    assert qs.shape == (B, H, npad // 32) and ks.shape == (B, H, npad // 64)
-    vc = G.unpermute_v(buf.v_codes.cpu().numpy(), N)
-    rvc, rvs = ref.vq
-    assert np.array_equal(buf.v_scale.cpu().numpy().view(np.uint32), rvs.view(np.uint32)), "v_scale"
-    assert np.array_equal(vc, rvc), "v_codes"
+    G.check_quant_bitexact(G.run_quant(G.gpu_case(case), fused), ref)
 
 
 def test_kappa_matches_binding():
