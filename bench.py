@@ -152,8 +152,60 @@ def cpu_baseline(case, rows_per_head=512, heads=None):
 def stats_ms(xs):
     xs = sorted(xs)
     pick = lambda p: xs[min(len(xs) - 1, int(round(p * (len(xs) - 1))))]
-    return {"mean": statistics.fmean(xs), "p50": pick(0.5), "p90": pick(0.9), "min": xs[0], "max": xs[-1],
-            "count": len(xs)}
+    return {"mean": statistics.fmean(xs), "p50": pick(0.5), "p90": pick(0.9), "p95": pick(0.95), "p99": pick(0.99),
+            "min": xs[0], "max": xs[-1], "count": len(xs)}
+
+
+class Sensors:
+    """Graphics clock and hotspot temperature of the GPU torch uses, read through
+    amdsmi (None where unavailable).  Matched to the device by PCI bus."""
+
+    def __init__(self, torch):
+        self.h, self.note = None, None
+        try:
+            import amdsmi
+            self.smi = amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            prop = torch.cuda.get_device_properties(0)
+            bus = getattr(prop, "pci_bus_id", None)
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)          # "dddd:bb:dd.f"
+                if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                    self.h = h
+            if self.h is None and len(handles) == 1:
+                self.h = handles[0]
+            if self.h is None:
+                self.note = "no amdsmi handle matched the device"
+        except Exception as e:          # sensors are context, never a failure
+            self.note = "amdsmi unavailable: %s" % type(e).__name__
+
+    def sample(self, stop, period, out):
+        """Append (host time, reading) every `period` seconds until stop is set."""
+        while not stop.is_set():
+            out.append((time.perf_counter(), self.read()))
+            stop.wait(period)
+
+    def read(self):
+        if self.h is None:
+            return None
+        out = {}
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, int) and 0 < c < 10000]
+            if clks:
+                out["gfxclk_mhz"] = statistics.fmean(clks)
+            elif isinstance(m.get("current_gfxclk"), int):
+                out["gfxclk_mhz"] = m["current_gfxclk"]
+            t = m.get("temperature_hotspot")
+            if isinstance(t, int):
+                out["hotspot_c"] = t
+            p = m.get("current_socket_power")
+            if isinstance(p, int):
+                out["socket_power_w"] = p
+        except Exception as e:
+            out["error"] = type(e).__name__
+        return out
 
 
 def main():
@@ -233,6 +285,47 @@ def main():
     attn_mean = statistics.fmean(at_ms)
     achieved = flops / (attn_mean * 1e-3) / 1e12
     qb = quant_bytes()
+
+    # the attention alone: 5 rounds x 10 launches; a host thread reads the graphics
+    # clock, hotspot temperature and socket power every 50 ms meanwhile (the
+    # driver's metrics table refreshes more slowly, so a reading can be stale)
+    import threading
+
+    sensors = Sensors(torch)
+    samples, stop = [], threading.Event()
+    sampler = threading.Thread(target=sensors.sample, args=(stop, 0.05, samples), daemon=True)
+    sampler.start()
+    for _ in range(40):            # about 1 s of load first, so the metrics table shows it
+        sage.sage_attn_fwd(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, out, sm,
+                           stream)
+    stream.synchronize()
+    rounds, all_round_ms = [], []
+    for _ in range(5):
+        t_begin = time.perf_counter()
+        er = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(10)]
+        for e in er:
+            e[0].record(stream)
+            sage.sage_attn_fwd(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, out, sm,
+                               stream)
+            e[1].record(stream)
+        stream.synchronize()
+        t_end = time.perf_counter()
+        ms = [e[0].elapsed_time(e[1]) for e in er]
+        all_round_ms += ms
+        inside = [r for t, r in samples if t_begin <= t <= t_end and r and "gfxclk_mhz" in r]
+        rounds.append({"ms": stats_ms(ms),
+                       "gfxclk_mhz": statistics.fmean(r["gfxclk_mhz"] for r in inside) if inside else None,
+                       "hotspot_c_max": max((r.get("hotspot_c", -1) for r in inside), default=None),
+                       "socket_power_w_max": max((r.get("socket_power_w", -1) for r in inside), default=None),
+                       "samples": len(inside)})
+    stop.set()
+    sampler.join(timeout=2.0)
+    # readings under full load only: socket power within 80 % of the highest seen
+    # (a stale reading from before the load shows far less power)
+    loaded = [r for t, r in samples if r and "gfxclk_mhz" in r and "socket_power_w" in r]
+    pmax = max((r["socket_power_w"] for r in loaded), default=0)
+    clk = [r["gfxclk_mhz"] for r in loaded if r["socket_power_w"] >= 0.8 * pmax]
+    sclk = statistics.fmean(clk) if clk else None
 
     # the pages' two quantisation stages as separate calls (same outputs)
     eqk = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
@@ -341,7 +434,12 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_i8f8_kernel", "achieved": achieved,
                      "peak": PEAK_I8F8_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_I8F8_TFLOPS,
                      "traffic": load_traffic(), "algorithmic_bytes": attn_bytes(),
-                     "flops_per_launch": flops, "ms_per_launch": attn_mean},
+                     "flops_per_launch": flops, "ms_per_launch": attn_mean,
+                     "sclk_mhz_measured": sclk,
+                     "peak_at_measured_sclk": None if sclk is None else 256 * 8192 * sclk * 1e6 / 1e12,
+                     "frac_at_measured_sclk": None if sclk is None else achieved / (256 * 8192 * sclk * 1e6 / 1e12),
+                     "peak_note": "5000 = published dense INT8/FP8 figure; 256 CU x 8192 ops/clk x 2.4 GHz = 5033"},
+        "attn_rounds": {"all": stats_ms(all_round_ms), "rounds": rounds, "sensor_note": sensors.note},
         "stages": {
             "qkv_quantize_ms": stats_ms(qkv_ms), "attn_fwd_ms": stats_ms(at_ms), "step_ms_events": stats_ms(step_ms),
             "qkv_quantize_GBps": (qb["qk_quantize"] + qb["v_quantize"]) / (statistics.fmean(qkv_ms) * 1e-3) / 1e9,
