@@ -88,9 +88,10 @@ def test_attn_mx_equals_mx_of_bf16_output(fmt, N):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
-def test_attn_mx_block24_equals_mx_of_bf16_output(fmt):
-    print("attn_mx block24 fmt", fmt, flush=True)
-    _, (c1, s1), (c2, s2), _ = _fused_vs_standalone(G.gpu_case(inputs.config("block24")), fmt)
+@pytest.mark.parametrize("name", ["block24", "stress"])
+def test_attn_mx_full_size_equals_mx_of_bf16_output(fmt, name):
+    print("attn_mx", name, "fmt", fmt, flush=True)
+    _, (c1, s1), (c2, s2), _ = _fused_vs_standalone(G.gpu_case(inputs.config(name)), fmt)
     assert torch.equal(s1, s2)
     assert torch.equal(c1, c2)
 

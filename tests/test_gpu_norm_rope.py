@@ -45,6 +45,7 @@ CASES = {
     "one_token": lambda: inputs.packed_case(1, 1, 1, seed=32),
     "n65": lambda: inputs.packed_case(1, 65, 4, seed=33),
     "block24": lambda: inputs.config("block24"),
+    "stress": lambda: inputs.config("stress"),        # B=2, x10 outlier channels, Student-t V
 }
 
 
