@@ -8,9 +8,9 @@
  * its stages and shapes but print no arithmetic:
  *   - "gb10-sampling-component-profile-1344x768-124f-seed440420.json",
  *     attention_internal_p50_milliseconds.sage2: qk_quantize, v_quantize,
- *     attention_forward, framework_and_k_smoothing_estimate (the four calls below
- *     are those stages; the K smoothing statistic is computed inside
- *     sage_quantize_qk);
+ *     attention_forward, framework_and_k_smoothing_estimate (sage_quantize_qk,
+ *     sage_quantize_v and sage_attn_fwd are those stages; the K smoothing
+ *     statistic is computed inside sage_quantize_qk);
  *   - "gb10-sage2-p0-interleave-softmax-latency.json", q_shape [1, 37810, 56, 128]
  *     and scheduler (64-key tiles, cta_k = 64; 32-query warps, warp_q = 32);
  *   - "gb10-sage-strided-nhd-summary-1344x768-124f-seed440420.json", dataflow:
@@ -21,6 +21,12 @@
  * amax / 127 and round-to-nearest-even, K smoothed by its per-head token mean,
  * OCP FP8 E4M3 V with per-channel scales amax / 448, an fp32 online softmax over
  * 64-key tiles, and P rounded to E4M3 (as 448 * p) for the FP8 P.V product.
+ *
+ * Around that path: sage_attn_fwd_bf16 (the unquantised path), sage_attn_fwd_int8qk
+ * (INT8 Q K^T with an unquantised P.V), sage_quantize_qkv (both quantisers in one
+ * call), sage_qk_norm_rope and sage_quantize_qkv_rope (the RMSNorm + RoPE step
+ * before quantisation, in place or fused), and sage_attn_fwd_mx / sage_mx_quantize
+ * (the output as OCP MX blocks for the projection after attention).
  *
  * Conventions for every entry point
  *   - Tensor pointers are DEVICE pointers; `stream` is a hipStream_t passed as
