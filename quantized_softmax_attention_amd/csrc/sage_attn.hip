@@ -86,7 +86,8 @@ __device__ __forceinline__ void tile_exp_chunk(const v16i (&s)[2], float c2, flo
         p[i] = fast_exp2(c2 * (float)s[kb][r + i] - bias);
         if (TAIL && 32 * kb + 8 * (r >> 2) + 4 * hl + i >= nvalid) p[i] = 0.0f;
     }
-    part += (p[0] + p[1]) + (p[2] + p[3]);
+    const float chunk = (p[0] + p[1]) + (p[2] + p[3]);
+    part = c == 0 ? chunk : part + chunk;   // (no add of the initial zero)
     // the low and then the high half of the dword; the previous tile's value
     // serves as the (fully overwritten) old operand, so no copy is needed
     int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pf[c], false);

@@ -66,7 +66,8 @@ __device__ __forceinline__ void tile_exp_chunk(const v16f (&s)[2], float c2, flo
         p[i] = fast_exp2(c2 * s[kb][r + i] - mnew);
         if (TAIL && 32 * kb + 8 * (r >> 2) + 4 * hl + i >= nvalid) p[i] = 0.0f;
     }
-    part += (p[0] + p[1]) + (p[2] + p[3]);
+    const float chunk = (p[0] + p[1]) + (p[2] + p[3]);
+    part = c == 0 ? chunk : part + chunk;   // (no add of the initial zero)
     const int ks = 2 * kb + (r >> 3), e0 = r & 7;
     pw[4 * ks + (e0 >> 1)] = pack_bf16(p[0], p[1]);
     pw[4 * ks + (e0 >> 1) + 1] = pack_bf16(p[2], p[3]);
