@@ -218,7 +218,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_i8f8_kernel(
     const int qb = (int)(id % (uint32_t)nqwg);
     const int64_t bh = id / (uint32_t)nqwg;
     const int b = (int)(bh / H), h = (int)(bh % H);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, hl = lane >> 5, ql = lane & 31;
+    const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: LDS addresses stay scalar
     const int q0 = qb * kQWg + 32 * w;
 
     // Q^T operand: lane (hl, ql) holds query q0+ql, channels 32*st + 16*hl .. +15.

@@ -135,7 +135,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bf16_kernel(View Q, View K, 
     const int qb = (int)(id % (uint32_t)nqwg);
     const int64_t bh = id / (uint32_t)nqwg;
     const int b = (int)(bh / H), h = (int)(bh % H);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6, hl = lane >> 5, ql = lane & 31;
+    const int t = threadIdx.x, lane = t & 63, hl = lane >> 5, ql = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(t >> 6);   // wave-uniform: LDS addresses stay scalar
     const int q0 = qb * kQWg + 32 * w;
     const int n = q0 + ql;
 
