@@ -46,6 +46,8 @@ int check_shape(int B, int N, int H, int D) {
     if (bytes > 4.0e18) return SAGE_ERR_SHAPE;
     const double blocks = (double)B * H * std::ceil((double)N / 128.0);
     if (blocks > 4.0e9) return SAGE_ERR_SHAPE;
+    // the quantisers' 1-D grids: one workgroup per (64-token block, head, batch)
+    if ((double)B * H * (double)(npad / 64) > 4.0e9) return SAGE_ERR_SHAPE;
     return SAGE_OK;
 }
 

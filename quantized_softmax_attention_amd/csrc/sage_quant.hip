@@ -12,6 +12,8 @@
 #include "sage_common.h"
 #include "sage_norm_rope.h"
 
+#include <utility>
+
 #pragma clang fp contract(off)
 
 namespace sage {
@@ -85,73 +87,145 @@ __device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (
 // partials as a pairwise tree in channel order (every lane ends with the same
 // bits: fp32 addition is commutative).  No contraction (see the pragma above):
 // every product and sum is rounded to fp32, so the result is bit-exactly
-// defined.  Must be called by all 16 lanes of the row; n is clamped by the caller
-// to a valid token (rows past N are discarded afterwards).
-__device__ __forceinline__ void norm_rope8(float (&x)[8], const float *__restrict__ gamma,
-                                           const float *__restrict__ rope, int n, float eps) {
-    const int seg = threadIdx.x & 15;
-    float a = x[0] * x[0];
+// defined.
+
+// Lane-permuted copy of a within each 16-lane row (DPP; all lanes active).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float a) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false));
+}
+
+// The xor butterfly over the 16 lanes of a row, partner offsets 1, 2, 4, 8, with
+// DPP: quad permutations reach the offset-1 and offset-2 partners; once each quad
+// holds one value, the half-row mirror reaches a lane of the offset-4 partner
+// quad, and once each half-row holds one value, the row mirror reaches the other
+// half.  Every step adds the same two values as the xor partner would.
+__device__ __forceinline__ float row16_sum(float a) {
+    a = a + dpp_f32<0xB1>(a);    // quad_perm [1, 0, 3, 2]: lane ^ 1
+    a = a + dpp_f32<0x4E>(a);    // quad_perm [2, 3, 0, 1]: lane ^ 2
+    a = a + dpp_f32<0x141>(a);   // row_half_mirror: the other quad of the half-row
+    a = a + dpp_f32<0x140>(a);   // row_mirror: the other half of the row
+    return a;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// 8 fp32 values as bf16 (round to nearest even: the conversion instruction), packed
+// in channel order.
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&x)[8]) {
+    auto pk = [](float a, float b) { return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b}); };
+    return make_uint4(pk(x[0], x[1]), pk(x[2], x[3]), pk(x[4], x[5]), pk(x[6], x[7]));
+}
+
+__device__ __forceinline__ void unpack_bf16x8(uint4 v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 1; j < 8; j++) a = a + x[j] * x[j];
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) a = a + __shfl_xor(a, o, 64);
-    const float r = 1.0f / __builtin_sqrtf(a / (float)kD + eps);
-    const float4 g0 = *reinterpret_cast<const float4 *>(gamma + 8 * seg);
-    const float4 g1 = *reinterpret_cast<const float4 *>(gamma + 8 * seg + 4);
-    const float4 *tr = reinterpret_cast<const float4 *>(rope + ((int64_t)n * (kD / 2) + 4 * seg) * 2);
-    const float4 t0 = tr[0], t1 = tr[1];
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-    const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-    float y[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) y[j] = (x[j] * r) * g[j];
-#pragma unroll
-    for (int p = 0; p < 4; p++) {
-        const float c = cs[2 * p], s = cs[2 * p + 1];
-        x[2 * p] = bf16_to_f32(f32_to_bf16(y[2 * p] * c - y[2 * p + 1] * s));
-        x[2 * p + 1] = bf16_to_f32(f32_to_bf16(y[2 * p] * s + y[2 * p + 1] * c));
+    for (int j = 0; j < 4; j++) {
+        x[2 * j] = __uint_as_float(w[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
     }
 }
 
-// The transformed row of token n (x as loaded; zeros stay zeros for n >= N).
-__device__ __forceinline__ void norm_rope_row(float (&x)[8], const float *__restrict__ gamma, const NormRope &nr,
-                                              int n, int N) {
-    norm_rope8(x, gamma, nr.rope, min(n, N - 1), nr.eps);
-    if (n >= N)
-#pragma unroll
-        for (int j = 0; j < 8; j++) x[j] = 0.0f;
+// v from lane I of this lane's 16-lane group (ds_swizzle bit mode within 32
+// lanes: source lane = (lane & 0x10) | I).
+template <int I>
+__device__ __forceinline__ float group_bcast(float v) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x10 | (I << 5)));
+}
+template <int... I>
+__device__ __forceinline__ void group_bcast_all(float v, float *out, std::integer_sequence<int, I...>) {
+    ((out[I] = group_bcast<I>(v)), ...);
 }
 
-__device__ __forceinline__ uint4 pack_bf16x8(const float (&x)[8]) {
-    return make_uint4(f32_to_bf16(x[0]) | (f32_to_bf16(x[1]) << 16), f32_to_bf16(x[2]) | (f32_to_bf16(x[3]) << 16),
-                      f32_to_bf16(x[4]) | (f32_to_bf16(x[5]) << 16), f32_to_bf16(x[6]) | (f32_to_bf16(x[7]) << 16));
+// The transform of R rows held by this lane (8 channels each; row i belongs to
+// token n[i] and uses weights gamma[i]), as bf16, zeros for tokens >= N.  Must be
+// called by all 16 lanes of the rows' group.  The factor r = 1/sqrt(ss/D + eps)
+// is evaluated once per row rather than once per lane: lane seg computes it for
+// row seg % R and every lane reads row i's from lane i of its 16-lane group (a
+// ds_swizzle broadcast); the value is the same, as every lane holds the same ss.
+template <int R>
+__device__ __forceinline__ void norm_rope_rows(float (&x)[R][8], const float *const (&gamma)[R], const int (&n)[R],
+                                               const NormRope &nr, int N, uint4 (&out)[R]) {
+    static_assert(R == 4 || R == 8, "rows per lane");
+    const int seg = threadIdx.x & 15;
+    float ss[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+        float a = x[i][0] * x[i][0];
+#pragma unroll
+        for (int j = 1; j < 8; j++) a = a + x[i][j] * x[i][j];
+        ss[i] = row16_sum(a);
+    }
+    float a = ss[0];
+#pragma unroll
+    for (int i = 1; i < R; i++) a = (seg % R == i) ? ss[i] : a;
+    const float rsel = 1.0f / __builtin_sqrtf(a / (float)kD + nr.eps);
+    float rr[R];
+    group_bcast_all(rsel, rr, std::make_integer_sequence<int, R>{});
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+        const float r = rr[i];
+        const float4 g0 = *reinterpret_cast<const float4 *>(gamma[i] + 8 * seg);
+        const float4 g1 = *reinterpret_cast<const float4 *>(gamma[i] + 8 * seg + 4);
+        const int nc = min(n[i], N - 1);
+        const float4 *tr = reinterpret_cast<const float4 *>(nr.rope + ((int64_t)nc * (kD / 2) + 4 * seg) * 2);
+        const float4 t0 = tr[0], t1 = tr[1];
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+        float y[8], z[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) y[j] = (x[i][j] * r) * g[j];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const float c = cs[2 * p], s = cs[2 * p + 1];
+            z[2 * p] = y[2 * p] * c - y[2 * p + 1] * s;
+            z[2 * p + 1] = y[2 * p] * s + y[2 * p + 1] * c;
+        }
+        out[i] = n[i] < N ? pack_bf16x8(z) : make_uint4(0, 0, 0, 0);
+    }
+}
+
+// The (64-token block, head, batch) of a workgroup in a 1-D grid of H * nblk * B
+// workgroups: heads vary fastest and the XCD remap hands each XCD a contiguous
+// range, so the workgroups of one token block, which read the same rows of the
+// rotary table, run on one XCD and find those rows in its L2.
+struct TokHead {
+    int tb, h, b;
+};
+__device__ __forceinline__ TokHead tok_head(int H, int nblk) {
+    const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    return TokHead{(int)((id / (uint32_t)H) % (uint32_t)nblk), (int)(id % (uint32_t)H),
+                   (int)(id / ((uint32_t)H * (uint32_t)nblk))};
 }
 
 // In place on the Q and K views: one workgroup per (64-token block, head,
 // batch); thread (row, seg) transforms tokens row + 16 i of both.  All loads
 // are issued before the first store (the views may share a buffer).
-__global__ __launch_bounds__(256) void norm_rope_kernel(OutView q, OutView k, int N, NormRope nr) {
-    const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(256) void norm_rope_kernel(OutView q, OutView k, int N, int H, NormRope nr) {
+    const TokHead w = tok_head(H, (N + 63) / 64);
+    const int tb = w.tb, h = w.h, b = w.b;
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
     uint16_t *qb = q.data + (int64_t)b * q.sb + (int64_t)h * q.sh + seg * 8;
     uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
-    float xq[4][8], xk[4][8];
+    float x[8][8];          // rows 0-3: Q of tokens row + 16 i; rows 4-7: K of the same tokens
+    int n[8];
+    const float *gamma[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int n = tb * 64 + row + 16 * i;
-        load_row8(qb + (int64_t)n * q.sn, n < N, xq[i]);
-        load_row8(kb + (int64_t)n * k.sn, n < N, xk[i]);
+        n[i] = n[4 + i] = tb * 64 + row + 16 * i;
+        gamma[i] = nr.gamma_q;
+        gamma[4 + i] = nr.gamma_k;
+        load_row8(qb + (int64_t)n[i] * q.sn, n[i] < N, x[i]);
+        load_row8(kb + (int64_t)n[i] * k.sn, n[i] < N, x[4 + i]);
     }
+    uint4 y[8];
+    norm_rope_rows<8>(x, gamma, n, nr, N, y);
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int n = tb * 64 + row + 16 * i;
-        norm_rope_row(xq[i], nr.gamma_q, nr, n, N);
-        norm_rope_row(xk[i], nr.gamma_k, nr, n, N);
-        if (n < N) {
-            *reinterpret_cast<uint4 *>(qb + (int64_t)n * q.sn) = pack_bf16x8(xq[i]);
-            *reinterpret_cast<uint4 *>(kb + (int64_t)n * k.sn) = pack_bf16x8(xk[i]);
+    for (int i = 0; i < 4; i++)
+        if (n[i] < N) {
+            *reinterpret_cast<uint4 *>(qb + (int64_t)n[i] * q.sn) = y[i];
+            *reinterpret_cast<uint4 *>(kb + (int64_t)n[i] * k.sn) = y[4 + i];
         }
-    }
 }
 
 // ------------------------------------------------------------- INT8 blocks
@@ -237,10 +311,17 @@ __device__ __forceinline__ void load_k_smoothed(View k, int b, int h, int tb, in
         const int n = tb * 64 + row + 16 * i;
         load_row8(kb + (int64_t)n * k.sn, n < N, x[i]);
     }
+    if (ROPE) {
+        const float *gamma[4] = {nr.gamma_k, nr.gamma_k, nr.gamma_k, nr.gamma_k};
+        const int n[4] = {tb * 64 + row, tb * 64 + row + 16, tb * 64 + row + 32, tb * 64 + row + 48};
+        uint4 y[4];
+        norm_rope_rows<4>(x, gamma, n, nr, N, y);
+#pragma unroll
+        for (int i = 0; i < 4; i++) unpack_bf16x8(y[i], x[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int n = tb * 64 + row + 16 * i;
-        if (ROPE) norm_rope_row(x[i], nr.gamma_k, nr, n, N);
 #pragma unroll
         for (int j = 0; j < 8; j++) x[i][j] = n < N ? x[i][j] - mean[j] : 0.0f;
     }
@@ -402,22 +483,29 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
     __shared__ float red[2][4];
     __shared__ uint4 kbuf[kKBlock][kD / 8];      // the block's K rows, bf16 (16 KB)
     __shared__ float vred[16][kD + 4];
-    const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const TokHead w = tok_head(H, (int)(Npad / 64));
+    const int tb = w.tb, h = w.h, b = w.b;
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
     const int64_t bh = (int64_t)b * H + h;
     // K and V rows (raw) of this thread: tokens row + 16 i; tokens >= N read as zero
     const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
     const uint16_t *vb = v.data + (int64_t)b * v.sb + (int64_t)h * v.sh + seg * 8;
     float vm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const int nt[4] = {tb * 64 + row, tb * 64 + row + 16, tb * 64 + row + 32, tb * 64 + row + 48};
+    if (ROPE) {
+        float xk[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) load_row8(kb + (int64_t)nt[i] * k.sn, nt[i] < N, xk[i]);
+        const float *gk[4] = {nr.gamma_k, nr.gamma_k, nr.gamma_k, nr.gamma_k};
+        uint4 y[4];
+        norm_rope_rows<4>(xk, gk, nt, nr, N, y);
+#pragma unroll
+        for (int i = 0; i < 4; i++) kbuf[row + 16 * i][seg] = y[i];
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int n = tb * 64 + row + 16 * i;
-        if (ROPE) {
-            float xk[8];
-            load_row8(kb + (int64_t)n * k.sn, n < N, xk);
-            norm_rope_row(xk, nr.gamma_k, nr, n, N);
-            kbuf[row + 16 * i][seg] = pack_bf16x8(xk);
-        } else {
+        const int n = nt[i];
+        if (!ROPE) {
             uint4 rk = make_uint4(0, 0, 0, 0);
             if (n < N) rk = *reinterpret_cast<const uint4 *>(kb + (int64_t)n * k.sn);
             kbuf[row + 16 * i][seg] = rk;
@@ -431,9 +519,13 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
     for (int j = 0; j < 8; j++) vred[row][seg * 8 + j] = vm[j];
     float xq[4][8];
     load_block(q, b, h, tb, N, xq);
-    if (ROPE)
+    if (ROPE) {
+        const float *gq[4] = {nr.gamma_q, nr.gamma_q, nr.gamma_q, nr.gamma_q};
+        uint4 y[4];
+        norm_rope_rows<4>(xq, gq, nt, nr, N, y);
 #pragma unroll
-        for (int i = 0; i < 4; i++) norm_rope_row(xq[i], nr.gamma_q, nr, tb * 64 + row + 16 * i, N);
+        for (int i = 0; i < 4; i++) unpack_bf16x8(y[i], xq[i]);
+    }
     float m[2];
     q_local_max(xq, m[0], m[1]);
     block_maxes(m, red);                             // its barriers also publish kbuf and vred
@@ -504,7 +596,8 @@ __global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, i
                                                         uint8_t *__restrict__ vc) {
     __shared__ float red[1][4];
     __shared__ uint32_t tile[kD][kTile / 4];
-    const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const TokHead w = tok_head(H, (int)(Npad / 64));
+    const int tb = w.tb, h = w.h, b = w.b;
     const int64_t bh = (int64_t)b * H + h;
     float xk[4][8];
     load_k_smoothed<ROPE>(k, b, h, tb, N, km, bh, nr, xk);
@@ -558,7 +651,7 @@ hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, cons
     float *wsv = reinterpret_cast<float *>(wsk + (int64_t)nchunk * total);
     float *amax = wsv + (int64_t)nchunk * total;
     const NormRope p = nr ? *nr : NormRope{};
-    const dim3 grid((unsigned)(Npad / 64), H, B);
+    const dim3 grid((unsigned)(Npad / 64 * H * B));
     // passes 1 and 3 run over every 64-token block of the padded code buffers
     // (blocks past N write zero codes and scales); the partials exist for the
     // nchunk blocks that hold tokens
@@ -580,7 +673,8 @@ hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, cons
 }
 
 hipError_t launch_norm_rope(OutView q, OutView k, int B, int N, int H, NormRope nr, hipStream_t stream) {
-    hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)((N + 63) / 64), H, B), dim3(256), 0, stream, q, k, N, nr);
+    hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)((N + 63) / 64 * H * B)), dim3(256), 0, stream, q, k, N, H,
+                       nr);
     return hipGetLastError();
 }
 
