@@ -434,14 +434,18 @@ __device__ __forceinline__ void v_tile_codes(View v, int b, int h, int tt, int N
 #pragma unroll
     for (int j = 0; j < 8; j++) sv[j] = vs[bh * kD + seg * 8 + j];
     uint32_t packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float x[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {             // all four rows in flight before any is encoded
+        const int n = tt * kTile + 4 * g + i;
+        load_row8(base + (int64_t)n * v.sn, n < N, x[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         const int n = tt * kTile + 4 * g + i;
-        float x[8];
-        load_row8(base + (int64_t)n * v.sn, n < N, x);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
-            const uint32_t code = (sv[j] == 0.0f || n >= N) ? 0u : e4m3_encode(x[j] / sv[j]);
+            const uint32_t code = (sv[j] == 0.0f || n >= N) ? 0u : e4m3_encode(x[i][j] / sv[j]);
             packed[j] |= code << (8 * i);
         }
     }
