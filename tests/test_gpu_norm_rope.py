@@ -117,3 +117,36 @@ def test_attention_over_fused_codes_matches_method():
     e = G.rel_l2(got, G.bf16_round(ref.method(rows)))
     print("attention after fused norm+rope quantisation: rel-L2 vs method oracle %.3e" % e, flush=True)
     assert e <= 1e-3
+
+
+def test_norm_rope_extreme_rows_bitexact():
+    # rows spanning the bf16 range, rows of zeros, single large or tiny entries,
+    # results in the bf16 subnormal range (tiny rows with a large eps): the
+    # in-place result and the fused codes stay bit-exact against the oracle
+    B, N, H, D = 1, 96, 3, 128
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((B, N, 3 * H, D))
+    scale = np.exp2(rng.integers(-100, 100, size=(B, N, 3 * H, 1)).astype(np.float64))
+    x = x * scale
+    x[0, 5] = 0.0                                    # a zero token (all heads of Q, K, V)
+    x[0, 6, :, 1:] = 0.0                             # one nonzero channel per row
+    x[0, 7] = 2.0 ** -133                            # bf16 subnormal inputs
+    x[0, 8, :, :64] = 3.0e38 / 128                   # large values
+    packed = torch.from_numpy(x.reshape(B, N, 3 * H * D)).float().to(torch.bfloat16)
+    HD = H * D
+    q, k, v = (packed[:, :, i * HD:(i + 1) * HD].unflatten(2, (H, D)) for i in range(3))
+    case = inputs.Case("extreme", B, N, H, D, q, k, v, packed)
+    for eps in (1e-6, 1e3):                          # a large eps pushes tiny rows into subnormals
+        nr = inputs.norm_rope_params(N, seed=9, eps=eps)
+        want = _oracle_transformed(case, nr)
+        g = G.gpu_case(case)
+        sage.sage_qk_norm_rope(g.q, g.k, nr.to("cuda").gamma_q, nr.to("cuda").gamma_k, nr.rope.cuda(), nr.eps)
+        torch.cuda.synchronize()
+        assert torch.equal(g.q.cpu().view(torch.int16), want.q.view(torch.int16)), ("Q", eps)
+        assert torch.equal(g.k.cpu().view(torch.int16), want.k.view(torch.int16)), ("K", eps)
+        ref = G.OracleRef(want)
+        g2 = G.gpu_case(case)
+        buf = sage.Buffers(B, N, H)
+        sage.quantize_qkv_rope(g2.q, g2.k, g2.v, nr.to("cuda"), buf)
+        torch.cuda.synchronize()
+        G.check_quant_bitexact(buf, ref)
