@@ -110,9 +110,20 @@ def load_traffic():
     return rec.get("traffic_bytes_per_launch")
 
 
+def cpu_model() -> str | None:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(case, rows_per_head=512, heads=None):
-    """Time the oracle: quantisers at full size, then the step-by-step
-    quantised attention on `rows_per_head` sampled rows (the last 64 plus
+    """Time the oracle: quantisers at full size (once on one core, then on all
+    cores), then the step-by-step quantised attention on `rows_per_head` sampled rows (the last 64 plus
     seeded random rows) of `heads` heads (all by default) against all keys,
     extrapolated to the whole call."""
     import numpy as np
@@ -122,12 +133,18 @@ def cpu_baseline(case, rows_per_head=512, heads=None):
     from tests.helpers import oracle_view
 
     q, k, v = (oracle_view(t) for t in (case.q, case.k, case.v))
-    t0 = time.perf_counter()
-    km = oracle.kmean(k)
-    qc, qs = oracle.quant_q(q, 32)
-    kc, ks = oracle.quant_k(k, km, 64)
-    vc, vs = oracle.quant_v(v)
-    t_quant = time.perf_counter() - t0
+    cores = oracle.num_threads()
+
+    def quantise():
+        t0 = time.perf_counter()
+        km = oracle.kmean(k)
+        res = oracle.quant_q(q, 32), oracle.quant_k(k, km, 64), oracle.quant_v(v)
+        return time.perf_counter() - t0, res
+
+    oracle.set_num_threads(1)
+    t_quant_1, _ = quantise()
+    oracle.set_num_threads(cores)
+    t_quant, ((qc, qs), (kc, ks), (vc, vs)) = quantise()
     heads = case.H if heads is None else heads
     rows = inputs.sample_rows(case.B, case.H, case.N, count=rows_per_head, tail=64)[:, :heads]
     sub = lambda a: np.ascontiguousarray(a[:, :heads])
@@ -140,8 +157,11 @@ def cpu_baseline(case, rows_per_head=512, heads=None):
         "value": attn_flops(case.B, case.N, case.H, case.D) / t_call / 1e12,
         "unit": "TFLOP/s",
         "ms_per_call_extrapolated": t_call * 1e3,
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
+        "quantisers_s_all_cores": t_quant,
+        "quantisers_s_one_core": t_quant_1,
+        "host": {"nproc": os.cpu_count(), "cpu_model": cpu_model()},
         "sample": ("quantisers at full size (%.2f s measured) + step-by-step quantised attention on %d sampled "
                    "rows x %d heads against all %d keys (%.2f s measured), attention time extrapolated x%.1f "
                    "to %d rows x %d heads" % (t_quant, rows_per_head, heads, case.N, t_attn, scale, case.N,

@@ -80,6 +80,8 @@ def _load():
         lib.sage_oracle_norm_rope_f64.restype = None
         lib.sage_oracle_attn_int8qk.argtypes = ([_p] * 4 + [_p, _i64, _i64, _i64] + [_int] * 7 +
                                                 [_dbl, _int, _p, _int, _p])
+        lib.sage_oracle_set_num_threads.argtypes = [_int]
+        lib.sage_oracle_set_num_threads.restype = None
         for f in ("sage_oracle_kmean", "sage_oracle_quant_q", "sage_oracle_quant_k", "sage_oracle_quant_v",
                   "sage_oracle_softmax_row", "sage_oracle_attn_exact", "sage_oracle_attn_method",
                   "sage_oracle_attn_int8qk",
@@ -131,6 +133,11 @@ def _c(a, dtype):
 def num_threads() -> int:
     """OpenMP threads the oracle's parallel loops use."""
     return int(_load().sage_oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Set the OpenMP threads of the following oracle calls."""
+    _load().sage_oracle_set_num_threads(int(n))
 
 
 # ------------------------------------------------------------------ codec

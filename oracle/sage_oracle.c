@@ -648,3 +648,13 @@ int sage_oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Threads for the following parallel loops (timing of the single-thread case). */
+void sage_oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
