@@ -200,6 +200,14 @@ class Sensors:
         except Exception as e:          # sensors are context, never a failure
             self.note = "amdsmi unavailable: %s" % type(e).__name__
 
+    def close(self):
+        if self.h is not None:
+            try:
+                self.smi.amdsmi_shut_down()
+            except Exception:
+                pass
+            self.h = None
+
     def sample(self, stop, period, out):
         """Append (host time, reading) every `period` seconds until stop is set."""
         while not stop.is_set():
@@ -340,6 +348,7 @@ def main():
                        "samples": len(inside)})
     stop.set()
     sampler.join(timeout=2.0)
+    sensors.close()
     # readings under full load only: socket power within 80 % of the highest seen
     # (a stale reading from before the load shows far less power)
     loaded = [r for t, r in samples if r and "gfxclk_mhz" in r and "socket_power_w" in r]
