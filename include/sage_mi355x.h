@@ -247,15 +247,17 @@ int sage_attn_fwd_int8qk(const int8_t *q_codes, const float *q_scale, const int8
  * Codes and scales are bit-exactly defined by the input values.
  *
  * sage_mx_quantize: the MX blocks of a bf16 [B, N, H, D] view (16-byte aligned,
- * strides multiples of 8).  codes 4-byte aligned.  fmt not one of the two
- * formats gives SAGE_ERR_VALUE. */
+ * strides multiples of 8).  codes 16-byte aligned (whole blocks are stored with
+ * 16-byte stores), scales any alignment.  fmt not one of the two formats gives
+ * SAGE_ERR_VALUE. */
 int sage_mx_quantize(const sage_bf16_in *x, int B, int N, int H, int D, int fmt, uint8_t *codes,
                      uint8_t *scales, void *stream);
 
 /* sage_attn_fwd with the output written as MX blocks instead of bf16: the
  * blocks of exactly the bf16 values sage_attn_fwd would write (so the result
  * equals sage_mx_quantize of that output, byte for byte).  Arguments as
- * sage_attn_fwd; codes/scales as sage_mx_quantize; rows >= N are not written. */
+ * sage_attn_fwd; codes and scales laid out as for sage_mx_quantize, codes 4-byte
+ * aligned; rows >= N are not written. */
 int sage_attn_fwd_mx(const int8_t *q_codes, const float *q_scale, const int8_t *k_codes,
                      const float *k_scale, const uint8_t *v_codes, const float *v_scale,
                      int B, int N, int H, int D, float sm_scale, int fmt, uint8_t *codes,
