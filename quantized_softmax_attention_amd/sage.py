@@ -234,6 +234,8 @@ def mx_out(B: int, N: int, H: int, fmt: int, device="cuda", D: int = HEAD_DIM):
 
 
 def _mx_shape(codes, scales, fmt):
+    if not (codes.is_contiguous() and scales.is_contiguous()):
+        raise ValueError("MX codes and scales are contiguous token-major buffers")
     B, N, per = codes.shape
     H = scales.shape[2] * 32 // HEAD_DIM
     assert per == (H * HEAD_DIM if fmt == MX_E4M3 else H * HEAD_DIM // 2)
@@ -299,8 +301,9 @@ def quantize_qkv_rope(q, k, v, nr, buf: Buffers, stream=None) -> None:
 
 
 def forward(q, k, v, out, buf: Buffers, sm_scale=None, stream=None) -> None:
-    """The quantised forward: quantize Q/K/V, then the fused attention into `out`."""
-    quantize(q, k, v, buf, stream)
+    """The quantised forward: quantize Q/K/V (one three-pass call), then the fused
+    attention into `out`."""
+    quantize_qkv(q, k, v, buf, stream)
     sage_attn_fwd(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, out, sm_scale, stream)
 
 
