@@ -235,9 +235,31 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ uint32_t int8_code(float x, float scale) {
+// The codes are defined on the IEEE quotient x / scale.  Per element it is
+// computed as x * inv corrected once (Markstein): with inv = RN(1/scale) (one
+// IEEE division per scale), q0 = RN(x * inv) and the exact residual
+// r = x - q0 * scale (an fma), RN(q0 + r * inv) is the correctly rounded quotient
+// whenever q0 and r stay normal; the sign of zero is restored.  For scales
+// >= kFastDivMin the residual can only underflow when |x / scale| < 2^-22, far
+// below the first boundary of either encoding (0.5 for INT8, 2^-10 for E4M3), so
+// the codes equal those of the IEEE quotient (tests/fast_div_check.c checks it on
+// every bf16 value and on random fp32 values, ties and subnormals, for scales
+// across the exponent range, codes of both formats).  Smaller scales use the IEEE
+// division.
+constexpr float kFastDivMin = 0x1p-80f;
+
+__device__ __forceinline__ float div_rn(float x, float scale, float inv) {
+    const float q0 = x * inv;
+    const float r = __builtin_fmaf(-q0, scale, x);
+    return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
+}
+
+// INT8 code of x / scale: ties to even, clamped to [-127, 127]; 0 when scale is 0.
+// FAST: scale >= kFastDivMin and inv = 1.0f / scale.
+template <bool FAST>
+__device__ __forceinline__ uint32_t int8_code(float x, float scale, float inv) {
     if (scale == 0.0f) return 0u;
-    float r = __builtin_rintf(x / scale);          // IEEE division, ties to even
+    float r = __builtin_rintf(FAST ? div_rn(x, scale, inv) : x / scale);
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (uint32_t)((int32_t)r) & 0xFFu;
 }
@@ -282,18 +304,29 @@ __device__ __forceinline__ float k_local_max(const float (&x)[4][8]) {
 }
 
 // Codes of the thread's 4 x 8 values with scale sc(i) for token row i.
-__device__ __forceinline__ void store_int8_codes(const float (&x)[4][8], float s_lo, float s_hi, int tb, int64_t bh,
-                                                 int64_t Npad, int8_t *__restrict__ codes) {
+template <bool FAST>
+__device__ __forceinline__ void store_int8_codes_as(const float (&x)[4][8], float s_lo, float s_hi, int tb,
+                                                    int64_t bh, int64_t Npad, int8_t *__restrict__ codes) {
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const float i_lo = FAST ? 1.0f / s_lo : 0.0f, i_hi = FAST ? 1.0f / s_hi : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float sc = i < 2 ? s_lo : s_hi;
+        const float sc = i < 2 ? s_lo : s_hi, inv = i < 2 ? i_lo : i_hi;
         uint32_t c[2] = {0, 0};
 #pragma unroll
-        for (int j = 0; j < 8; j++) c[j >> 2] |= int8_code(x[i][j], sc) << (8 * (j & 3));
+        for (int j = 0; j < 8; j++) c[j >> 2] |= int8_code<FAST>(x[i][j], sc, inv) << (8 * (j & 3));
         const int64_t off = (bh * Npad + (int64_t)tb * 64 + row + 16 * i) * kD + seg * 8;
         *reinterpret_cast<uint2 *>(codes + off) = make_uint2(c[0], c[1]);
     }
+}
+
+// The scales are workgroup-uniform, so one of the two paths runs.
+__device__ __forceinline__ void store_int8_codes(const float (&x)[4][8], float s_lo, float s_hi, int tb, int64_t bh,
+                                                 int64_t Npad, int8_t *__restrict__ codes) {
+    if (s_lo >= kFastDivMin && s_hi >= kFastDivMin)
+        store_int8_codes_as<true>(x, s_lo, s_hi, tb, bh, Npad, codes);
+    else
+        store_int8_codes_as<false>(x, s_lo, s_hi, tb, bh, Npad, codes);
 }
 
 // K of the block, smoothed: x = fp32(k) - k_mean (one fp32 subtraction); zero
@@ -440,13 +473,29 @@ __device__ __forceinline__ void v_tile_codes(View v, int b, int h, int tt, int N
         const int n = tt * kTile + 4 * g + i;
         load_row8(base + (int64_t)n * v.sn, n < N, x[i]);
     }
+    bool fast = true;                         // every channel scale of this thread large enough
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int n = tt * kTile + 4 * g + i;
+    for (int j = 0; j < 8; j++) fast = fast && sv[j] >= kFastDivMin;
+    if (fast) {
+        float inv[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            const uint32_t code = (sv[j] == 0.0f || n >= N) ? 0u : e4m3_encode(x[i][j] / sv[j]);
-            packed[j] |= code << (8 * i);
+        for (int j = 0; j < 8; j++) inv[j] = 1.0f / sv[j];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int n = tt * kTile + 4 * g + i;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+                packed[j] |= (n >= N ? 0u : e4m3_encode(div_rn(x[i][j], sv[j], inv[j]))) << (8 * i);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int n = tt * kTile + 4 * g + i;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                const uint32_t code = (sv[j] == 0.0f || n >= N) ? 0u : e4m3_encode(x[i][j] / sv[j]);
+                packed[j] |= code << (8 * i);
+            }
         }
     }
     const int p0 = 32 * (g & 1) + 16 * (g >> 3) + 4 * ((g >> 1) & 3);
