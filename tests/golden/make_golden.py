@@ -1,5 +1,7 @@
 """Write tests/golden/tiny_oracle.json: digests and a few values of the oracle's
-results on the tiny workload (B=1, N=256, H=2, D=128, seed 0).  Calls only the
+results on the tiny workload (B=1, N=256, H=2, D=128, seed 0): quantisers, the
+exact, method and INT8-QK/bf16-PV attention, MX blocks of the method's output
+and the RMSNorm + RoPE transform of Q and K.  Calls only the
 oracle (and the seeded input generators).  Re-run only when a change to the
 oracle's arithmetic is justified by the method's definition.
 
@@ -35,6 +37,13 @@ def compute():
     vc, vs = oracle.quant_v(v)
     exact = oracle.attn_exact(q, k, v, sm)
     method = oracle.attn_method(qc, qs, kc, ks, vc, vs, sm)
+    i8qk = oracle.attn_int8qk(qc, qs, kc, ks, v, sm)
+    tok = np.ascontiguousarray(method.transpose(0, 2, 1, 3)).reshape(c.B, c.N, c.H * c.D)
+    mx8c, mx8s = oracle.mx_quantize(tok, oracle.MX_E4M3)
+    mx4c, mx4s = oracle.mx_quantize(tok, oracle.MX_E2M1)
+    nr = inputs.norm_rope_params(c.N, seed=1)
+    tq = oracle.norm_rope(q, nr.gamma_q.numpy(), nr.rope.numpy(), nr.eps)
+    tk = oracle.norm_rope(k, nr.gamma_k.numpy(), nr.rope.numpy(), nr.eps)
     return {
         "inputs_sha256": {n: digest(t.contiguous().float().numpy())
                           for n, t in (("q", c.q), ("k", c.k), ("v", c.v))},
@@ -44,6 +53,11 @@ def compute():
         "exact_row0_head0_first8": [float(x) for x in exact[0, 0, 0, :8]],
         "method_row0_head0_first8": [float(x) for x in method[0, 0, 0, :8]],
         "method_vs_exact_rel_l2": oracle.rel_l2(method, exact),
+        "int8qk_row0_head0_first8": [float(x) for x in i8qk[0, 0, 0, :8]],
+        "int8qk_vs_exact_rel_l2": oracle.rel_l2(i8qk, exact),
+        "mx_e4m3_codes_sha256": digest(mx8c), "mx_e4m3_scales_sha256": digest(mx8s),
+        "mx_e2m1_codes_sha256": digest(mx4c), "mx_e2m1_scales_sha256": digest(mx4s),
+        "norm_rope_q_sha256": digest(tq), "norm_rope_k_sha256": digest(tk),
     }
 
 
