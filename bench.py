@@ -248,8 +248,8 @@ def main():
                     help="also launch one plain 1 GiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path (heads would shard with no "
-              "exchange; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the heads would shard across GPUs "
+              "with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch
