@@ -64,6 +64,21 @@ def test_mx_quantize_strided_view(fmt):
     assert np.array_equal(codes.cpu().numpy(), wc)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mx_quantize_hnd_view(fmt):
+    # heads outermost ([B, H, N, D] storage viewed as [B, N, H, D])
+    B, N, H = 2, 130, 3
+    x = inputs.mx_tensor(B, N, H, seed=9)
+    hnd = x.transpose(1, 2).contiguous().cuda().transpose(1, 2)
+    codes, scales = sage.mx_out(B, N, H, fmt)
+    _fill(codes, scales)
+    sage.sage_mx_quantize(hnd, fmt, codes, scales)
+    torch.cuda.synchronize()
+    wc, ws = _mx_oracle(x, fmt)
+    assert np.array_equal(scales.cpu().numpy(), ws)
+    assert np.array_equal(codes.cpu().numpy(), wc)
+
+
 def _fused_vs_standalone(gcase, fmt, buf=None):
     out, buf = G.run_attn(gcase, buf)
     B, N, H = gcase.B, gcase.N, gcase.H
