@@ -356,6 +356,20 @@ def main():
     clk = [r["gfxclk_mhz"] for r in loaded if r["socket_power_w"] >= 0.8 * pmax]
     sclk = statistics.fmean(clk) if clk else None
 
+    # practical HBM ceiling for the quantisers: a plain 1 GiB device-to-device copy
+    ca = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cb = torch.empty_like(ca)
+    ec = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(5)]
+    with torch.cuda.stream(stream):
+        cb.copy_(ca)
+        for e in ec:
+            e[0].record(stream)
+            cb.copy_(ca)
+            e[1].record(stream)
+    stream.synchronize()
+    copy_ms = statistics.median(e[0].elapsed_time(e[1]) for e in ec)
+    del ca, cb
+
     # the pages' two quantisation stages as separate calls (same outputs)
     eqk = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for e in eqk:
@@ -476,6 +490,7 @@ def main():
             "qk_quantize_GBps": qb["qk_quantize"] / (statistics.fmean(qk_ms) * 1e-3) / 1e9,
             "v_quantize_GBps": qb["v_quantize"] / (statistics.fmean(v_ms) * 1e-3) / 1e9,
             "hbm_peak_GBps": PEAK_HBM_GBS,
+            "copy_1GiB_GBps": 2 * (1 << 30) / (copy_ms * 1e-3) / 1e9,   # read + write of a plain device copy
             "attn_pct_of_i8f8_peak": 100.0 * achieved / PEAK_I8F8_TFLOPS,
             "step_pct_of_i8f8_peak": 100.0 * value / PEAK_I8F8_TFLOPS,
         },
