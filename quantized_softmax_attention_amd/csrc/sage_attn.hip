@@ -11,7 +11,7 @@
 //    v_mfma_i32_32x32x32_i8, the 32x32 accumulator gives each lane ONE query
 //    (lane % 32) and 16 keys, so row maxima and sums are in-lane reductions plus
 //    one exchange between lane l and l^32.  The same lane then holds exactly the
-//    P^T values the B operand of v_mfma_scale_f32_32x32x64_f8f6f4 needs (32 keys
+//    P^T values the B operand of the FP8 MFMA (32x32x64, E4M3 x E4M3) needs (32 keys
 //    of one query), so P never travels through LDS.  V codes are stored by the
 //    quantiser with the matching key order (kappa in the public header).
 //  * One wave = 32 queries (one Q scale block) x 64 keys (one K scale block) per
@@ -94,7 +94,10 @@ __device__ __forceinline__ void tile_exp_chunk(const v16i (&s)[2], float c2, flo
     pf[c] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wd, true);
 }
 
-// O^T += V^T P^T, 32 channels per MFMA.
+// O^T += V^T P^T, 32 channels per MFMA.  The block-scale operands of the builtin
+// are given as 0, which selects the unscaled v_mfma_f32_32x32x64_f8f6f4 (the same
+// products as E8M0 scales of 127, i.e. 1.0; the shorter encoding carries no scale
+// registers).
 __device__ __forceinline__ void pv_tile(const v4i *lv, const v8i &pf, int hl, int ql, v16f (&o)[4]) {
 #pragma unroll
     for (int db = 0; db < 4; db++) {
@@ -102,7 +105,7 @@ __device__ __forceinline__ void pv_tile(const v4i *lv, const v8i &pf, int hl, in
         v4i lo = lv[v_slot(d, 2 * hl)];
         v4i hi = lv[v_slot(d, 2 * hl + 1)];
         v8i va = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf, o[db], 0, 0, 0, 127, 0, 127);
+        o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pf, o[db], 0, 0, 0, 0, 0, 0);
     }
 }
 
@@ -147,7 +150,7 @@ __device__ __forceinline__ void step(v16i (&s)[2], v16i (&sn)[2], const v4i *lk_
         for (int db = 0; db < 4; db++) {
             if (db < 3) va[(db + 1) & 1] = v_operand(lv_prev, db + 1, hl, ql);
             if (QK && db >= 2) ka[db - 2] = k8_operand(lk_next, db - 2, hl, ql);
-            o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db & 1], st.pf, o[db], 0, 0, 0, 127, 0, 127);
+            o[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va[db & 1], st.pf, o[db], 0, 0, 0, 0, 0, 0);
         }
     }
     const float mnew = tile_max_i32<TAIL>(s, c2, nvalid, hl, st.m2);
