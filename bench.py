@@ -458,6 +458,30 @@ def main():
                     "unfused_ms": attn_mean + statistics.fmean(alone)}
         del codes, scales
 
+    # one GPU's share of an 8-way head split: 7 heads of the same buffer (strided
+    # views of their columns), writing their slice of the token-major output
+    hs = slice(0, H // 8)
+    sbuf = sage.Buffers(B, N, H // 8, device=dev)
+    es = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.bf16_calls)]
+    sage.forward(g.q[:, :, hs], g.k[:, :, hs], g.v[:, :, hs], out[:, :, hs], sbuf, sm, stream)
+    for e in es:
+        e[0].record(stream)
+        sage.quantize_qkv(g.q[:, :, hs], g.k[:, :, hs], g.v[:, :, hs], sbuf, stream)
+        e[1].record(stream)
+        sage.sage_attn_fwd(sbuf.q_codes, sbuf.q_scale, sbuf.k_codes, sbuf.k_scale, sbuf.v_codes, sbuf.v_scale,
+                           out[:, :, hs], sm, stream)
+        e[2].record(stream)
+    stream.synchronize()
+    s_q = [e[0].elapsed_time(e[1]) for e in es]
+    s_a = [e[1].elapsed_time(e[2]) for e in es]
+    f7 = attn_flops(h=H // 8)
+    n_wg = -(-N // 128) * (H // 8) * B
+    shard = {"heads": H // 8, "qkv_quantize_ms": stats_ms(s_q), "attn_fwd_ms": stats_ms(s_a),
+             "attn_tflops": f7 / (statistics.fmean(s_a) * 1e-3) / 1e12,
+             "attn_workgroups": n_wg, "workgroup_rounds": n_wg / (2 * 256),
+             "note": "per-GPU share of an 8-way head split, measured on one GPU; no multi-GPU run"}
+    del sbuf
+
     line = {
         "metric": METRIC,
         "value": value,
@@ -503,6 +527,7 @@ def main():
                         "peak_note": "half the ops at the INT8 peak, half at the BF16 peak: 1/(0.5/5000 + 0.5/2500)"},
         "rope_path": rope,
         "mx_path": mx,
+        "head_shard": shard,
         "pages_context": {"gb10_attention_forward_p50_ms": 238.995, "gb10_total_excluding_layout_ms": 258.613,
                           "note": "NVIDIA GB10 on real activations; context only"},
         "input_generation_s": gen_s,

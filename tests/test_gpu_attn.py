@@ -127,3 +127,31 @@ def test_attn_rows_beyond_n_untouched():
     torch.cuda.synchronize()
     assert torch.all(big[:, 70:] == 7.0)
     assert torch.isfinite(big[:, :70].float()).all()
+
+
+@pytest.mark.parametrize("shard", [0, 7])
+def test_head_shard_equals_full_call(shard):
+    # Heads are independent (every statistic and scale is per head), so one GPU's
+    # share of an 8-way head split -- 7 heads of the block-24 buffer, as strided
+    # views of its columns, writing their slice of the token-major output -- gives
+    # the same codes, scales and output bytes as the 56-head call.
+    print("head shard", shard, flush=True)
+    case = G.gpu_case(inputs.config("block24"))
+    full = sage.Buffers(case.B, case.N, case.H)
+    sage.quantize_qkv(case.q, case.k, case.v, full)
+    out_full = sage.token_major_out(case.B, case.N, case.H)
+    sage.sage_attn_fwd(full.q_codes, full.q_scale, full.k_codes, full.k_scale, full.v_codes, full.v_scale,
+                       out_full, G.SM)
+    hs = slice(7 * shard, 7 * shard + 7)
+    part = sage.Buffers(case.B, case.N, 7)
+    sage.quantize_qkv(case.q[:, :, hs], case.k[:, :, hs], case.v[:, :, hs], part)
+    out_part = torch.full_like(out_full, 3.0)
+    sage.sage_attn_fwd(part.q_codes, part.q_scale, part.k_codes, part.k_scale, part.v_codes, part.v_scale,
+                       out_part[:, :, hs], G.SM)
+    torch.cuda.synchronize()
+    for f in ("q_codes", "q_scale", "k_codes", "k_scale", "k_mean", "v_codes", "v_scale"):
+        assert torch.equal(getattr(part, f), getattr(full, f)[:, hs]), f
+    assert torch.equal(out_part[:, :, hs].view(torch.int16), out_full[:, :, hs].view(torch.int16))
+    rest = torch.ones(case.H, dtype=torch.bool)
+    rest[hs] = False
+    assert torch.all(out_part[:, :, rest] == 3.0)
