@@ -44,26 +44,73 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(View k, int N, int H
     for (int j = 0; j < 8; j++) dst[j] = s[j];
 }
 
-// Total over chunks in ascending order, one fp64 division by N, one rounding.
-// The adds are a dependent chain, so loads are issued 32 at a time ahead of it.
-__global__ __launch_bounds__(256) void kmean_final_kernel(const double *__restrict__ ws, int N, int H,
-                                                          int nchunk, int B, float *__restrict__ km) {
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int64_t HD = (int64_t)H * kD;
-    if (i >= (int64_t)B * HD) return;
-    int64_t b = i / HD, hd = i % HD;
-    const double *p = ws + b * nchunk * HD + hd;
+// ------------------------------------------- reductions over chunk partials
+// The per-chunk partials (fp64 K column sums and/or fp32 V column maxima) are
+// rows of H*kD values, one row per chunk of tokens, for each batch entry.  One
+// workgroup reduces 32 columns over all chunks: its 256 threads stage 64 chunk
+// rows at a time in LDS (thread t loads rows t/32 + 8j of column t%32, so each
+// load is a 256-byte row segment per 32 lanes, and sixteen loads per thread are
+// in flight), double buffered so the next rows load while this batch is reduced;
+// lanes 0..31 of wave 0 add their column's sums in ascending chunk order (the
+// order the K mean is defined in), lanes 32..63 take the maxima (exact in any
+// order).  Results: km = (float)(sum / N) (one fp64 division, one rounding);
+// amax and v_scale = amax / 448.
+constexpr int kColsPerWg = 32;
+constexpr int kRowsPerBatch = 64;
+
+template <bool SUM, bool MAX>
+__global__ __launch_bounds__(256) void chunk_final_kernel(const double *__restrict__ wsk,
+                                                          const float *__restrict__ wsv, int N, int H,
+                                                          int nchunk, float *__restrict__ km,
+                                                          float *__restrict__ amax, float *__restrict__ vs) {
+    __shared__ double lk[SUM ? 2 : 1][SUM ? kRowsPerBatch : 1][kColsPerWg];
+    __shared__ float lv[MAX ? 2 : 1][MAX ? kRowsPerBatch : 1][kColsPerWg];
+    const int t = threadIdx.x, col = t % kColsPerWg, r0 = t / kColsPerWg;
+    const int64_t HD = (int64_t)H * kD;
+    const int wpb = 4 * H;                                         // workgroups per batch entry
+    const int b = (int)(blockIdx.x / wpb);
+    const int64_t c0 = (int64_t)(blockIdx.x % wpb) * kColsPerWg;   // first column of this workgroup
+    const double *pk = SUM ? wsk + (int64_t)b * nchunk * HD + c0 + col : nullptr;
+    const float *pv = MAX ? wsv + (int64_t)b * nchunk * HD + c0 + col : nullptr;
+    const int nb = (nchunk + kRowsPerBatch - 1) / kRowsPerBatch;
+    double xk[kRowsPerBatch / 8];
+    float xv[kRowsPerBatch / 8];
+    auto load = [&](int batch) {
+#pragma unroll
+        for (int j = 0; j < kRowsPerBatch / 8; j++) {
+            const int c = batch * kRowsPerBatch + r0 + 8 * j;
+            if (SUM) xk[j] = c < nchunk ? pk[(int64_t)c * HD] : 0.0;
+            if (MAX) xv[j] = c < nchunk ? pv[(int64_t)c * HD] : 0.0f;
+        }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < kRowsPerBatch / 8; j++) {
+            if (SUM) lk[buf][r0 + 8 * j][col] = xk[j];
+            if (MAX) lv[buf][r0 + 8 * j][col] = xv[j];
+        }
+    };
+    load(0);
+    store(0);
+    __syncthreads();
     double s = 0.0;
-    int c = 0;
-    for (; c + 32 <= nchunk; c += 32) {
-        double v[32];
-#pragma unroll
-        for (int j = 0; j < 32; j++) v[j] = p[(int64_t)(c + j) * HD];
-#pragma unroll
-        for (int j = 0; j < 32; j++) s += v[j];
+    float a = 0.0f;
+    for (int i = 0; i < nb; i++) {
+        if (i + 1 < nb) load(i + 1);
+        const int rows = min(kRowsPerBatch, nchunk - i * kRowsPerBatch);
+        if (SUM && t < kColsPerWg)
+            for (int r = 0; r < rows; r++) s += lk[i & 1][r][t];
+        if (MAX && t >= kColsPerWg && t < 2 * kColsPerWg)
+            for (int r = 0; r < rows; r++) a = fmaxf(a, lv[i & 1][r][t - kColsPerWg]);
+        if (i + 1 < nb) store((i + 1) & 1);
+        __syncthreads();
     }
-    for (; c < nchunk; c++) s += p[(int64_t)c * HD];
-    km[i] = (float)(s / (double)N);
+    const int64_t o = (int64_t)b * HD + c0;
+    if (SUM && t < kColsPerWg) km[o + t] = (float)(s / (double)N);
+    if (MAX && t >= kColsPerWg && t < 2 * kColsPerWg) {
+        amax[o + t - kColsPerWg] = a;
+        vs[o + t - kColsPerWg] = a / 448.0f;
+    }
 }
 
 // 8 consecutive channels of one token row (a 16-byte load), widened exactly.
@@ -429,29 +476,6 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(View v, int N, int 
     }
 }
 
-// Channel amax over chunks -> amax[b][h][d] and v_scale = amax / 448.
-__global__ __launch_bounds__(256) void v_amax_final_kernel(const float *__restrict__ ws, int H, int nchunk,
-                                                           int B, float *__restrict__ amax,
-                                                           float *__restrict__ vs) {
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    int64_t HD = (int64_t)H * kD;
-    if (i >= (int64_t)B * HD) return;
-    int64_t b = i / HD, hd = i % HD;
-    const float *p = ws + b * nchunk * HD + hd;
-    float a = 0.0f;
-    int c = 0;
-    for (; c + 32 <= nchunk; c += 32) {   // loads issued 32 at a time (max is exact in any order)
-        float v[32];
-#pragma unroll
-        for (int j = 0; j < 32; j++) v[j] = p[(int64_t)(c + j) * HD];
-#pragma unroll
-        for (int j = 0; j < 32; j++) a = fmaxf(a, v[j]);
-    }
-    for (; c < nchunk; c++) a = fmaxf(a, p[(int64_t)c * HD]);
-    amax[i] = a;
-    vs[i] = a / 448.0f;
-}
-
 // The E4M3 codes of one 64-key tile tt of one head, written tile-major.  Thread
 // (g = tid/16, seg = tid%16) encodes keys 4g..4g+3 of channels 8*seg..+7.  The
 // four codes of one channel land in consecutive bytes p0..p0+3 of the tile row,
@@ -606,42 +630,6 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
     }
 }
 
-// k_mean and the V channel maxima and scales from the pass-1 partials.
-__global__ __launch_bounds__(256) void qkv_final_kernel(const double *__restrict__ wsk, const float *__restrict__ wsv,
-                                                        int N, int H, int nchunk, int B, float *__restrict__ km,
-                                                        float *__restrict__ amax, float *__restrict__ vs) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t HD = (int64_t)H * kD;
-    if (i >= (int64_t)B * HD) return;
-    const int64_t b = i / HD, hd = i % HD;
-    const double *pk = wsk + b * nchunk * HD + hd;
-    const float *pv = wsv + b * nchunk * HD + hd;
-    double s = 0.0;
-    float a = 0.0f;
-    int c = 0;
-    for (; c + 16 <= nchunk; c += 16) {   // loads issued 16 at a time ahead of the ordered adds
-        double x[16];
-        float y[16];
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            x[j] = pk[(int64_t)(c + j) * HD];
-            y[j] = pv[(int64_t)(c + j) * HD];
-        }
-#pragma unroll
-        for (int j = 0; j < 16; j++) {
-            s += x[j];
-            a = fmaxf(a, y[j]);
-        }
-    }
-    for (; c < nchunk; c++) {
-        s += pk[(int64_t)c * HD];
-        a = fmaxf(a, pv[(int64_t)c * HD]);
-    }
-    km[i] = (float)(s / (double)N);
-    amax[i] = a;
-    vs[i] = a / 448.0f;
-}
-
 template <bool ROPE>
 __global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, int H, int64_t Npad, NormRope nr,
                                                         const float *__restrict__ km, const float *__restrict__ vs,
@@ -663,6 +651,11 @@ __global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, i
 }
 
 // ------------------------------------------------------------ launchers
+// chunk_final_kernel: kD / kColsPerWg = 4 workgroups per head and batch entry (the
+// shape check bounds B*H by 1e9, so the 1-D grid fits).
+static_assert(kD == 4 * kColsPerWg, "four column groups per head");
+static dim3 final_grid(int B, int H) { return dim3((unsigned)(4 * (int64_t)H * B)); }
+
 hipError_t launch_quantize_qk(View q, View k, int B, int N, int H, int8_t *qc, float *qs, int8_t *kc,
                               float *ks, float *km, void *workspace, hipStream_t stream) {
     const int nchunk = (N + kSumChunk - 1) / kSumChunk;
@@ -670,9 +663,8 @@ hipError_t launch_quantize_qk(View q, View k, int B, int N, int H, int8_t *qc, f
     double *ws = static_cast<double *>(workspace);
     hipLaunchKernelGGL(kmean_partial_kernel, dim3((nchunk + 15) / 16, H, B), dim3(256), 0, stream, k, N, H, nchunk,
                        ws);
-    int64_t total = (int64_t)B * H * kD;
-    hipLaunchKernelGGL(kmean_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, ws, N,
-                       H, nchunk, B, km);
+    hipLaunchKernelGGL((chunk_final_kernel<true, false>), final_grid(B, H), dim3(256), 0, stream, ws, nullptr, N, H,
+                       nchunk, km, nullptr, nullptr);
     hipLaunchKernelGGL(quant_qk_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, q, k, N, H,
                        Npad, km, qc, qs, kc, ks);
     return hipGetLastError();
@@ -685,9 +677,8 @@ hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs
     float *part = static_cast<float *>(workspace);
     float *amax = part + (int64_t)nchunk * B * H * kD;
     hipLaunchKernelGGL(v_amax_partial_kernel, dim3(nchunk, H, B), dim3(256), 0, stream, v, N, H, nchunk, part);
-    int64_t total = (int64_t)B * H * kD;
-    hipLaunchKernelGGL(v_amax_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, part, H,
-                       nchunk, B, amax, vs);
+    hipLaunchKernelGGL((chunk_final_kernel<false, true>), final_grid(B, H), dim3(256), 0, stream, nullptr, part, N,
+                       H, nchunk, nullptr, amax, vs);
     hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)(Npad / kTile), H, B), dim3(256), 0, stream, v, N, H, Npad,
                        vs, vc);
     return hipGetLastError();
@@ -714,8 +705,8 @@ hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, cons
     else
         hipLaunchKernelGGL(qkv_pass1_kernel<false>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
                            wsk, wsv);
-    hipLaunchKernelGGL(qkv_final_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, wsk, wsv, N,
-                       H, nchunk, B, km, amax, vs);
+    hipLaunchKernelGGL((chunk_final_kernel<true, true>), final_grid(B, H), dim3(256), 0, stream, wsk, wsv, N, H,
+                       nchunk, km, amax, vs);
     if (nr)
         hipLaunchKernelGGL(qkv_pass3_kernel<true>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
                            vc);
