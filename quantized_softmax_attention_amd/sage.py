@@ -121,6 +121,59 @@ def bf16_out(t: torch.Tensor) -> BF16Out:
     return BF16Out(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
 
 
+def _on_gpu(name: str, t) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s: expected a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s: the library takes device memory; got a tensor on %s" % (name, t.device))
+
+
+def _need(name: str, t, dtype, count: int) -> None:
+    """A library-layout buffer: on the GPU, of `dtype`, contiguous, with at
+    least `count` elements (the kernels write every one of them)."""
+    _on_gpu(name, t)
+    if t.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s: expected a contiguous buffer" % name)
+    if t.numel() < count:
+        raise ValueError("%s: holds %d elements, %d needed" % (name, t.numel(), count))
+
+
+def _same_device(*tensors) -> None:
+    devs = {t.device for t in tensors if isinstance(t, torch.Tensor)}
+    if len(devs) > 1:
+        raise ValueError("all tensors of one call must be on one GPU; got %s" % sorted(map(str, devs)))
+
+
+def _views(shape, **views) -> None:
+    for name, t in views.items():
+        _on_gpu(name, t)
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError("%s: shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+
+
+def _codes(B: int, N: int, H: int, D: int, q_codes=None, q_scale=None, k_codes=None, k_scale=None, k_mean=None,
+           v_codes=None, v_scale=None) -> None:
+    """Size, type and placement checks of the code and scale buffers (the C ABI
+    takes their pointers as given, so an undersized buffer would be overrun)."""
+    npad = (N + N_ALIGN - 1) // N_ALIGN * N_ALIGN
+    spec = {"q_codes": (q_codes, torch.int8, B * H * npad * D), "q_scale": (q_scale, torch.float32,
+            B * H * npad // Q_BLOCK), "k_codes": (k_codes, torch.int8, B * H * npad * D),
+            "k_scale": (k_scale, torch.float32, B * H * npad // K_BLOCK), "k_mean": (k_mean, torch.float32, B * H * D),
+            "v_codes": (v_codes, torch.uint8, B * H * npad * D), "v_scale": (v_scale, torch.float32, B * H * D)}
+    for name, (t, dtype, count) in spec.items():
+        if t is not None:
+            _need(name, t, dtype, count)
+
+
+def _workspace(t) -> int:
+    _on_gpu("workspace", t)
+    if not t.is_contiguous():
+        raise ValueError("workspace: expected a contiguous buffer")
+    return t.numel() * t.element_size()
+
+
 def sage_npad(N: int) -> int:
     return int(lib().sage_npad(N))
 
@@ -135,18 +188,25 @@ def sage_v_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
 
 def sage_quantize_qk(q, k, q_codes, q_scale, k_codes, k_scale, k_mean, workspace, stream=None) -> None:
     B, N, H, D = _shape(q)
+    _views((B, N, H, D), q=q, k=k)
+    _codes(B, N, H, D, q_codes=q_codes, q_scale=q_scale, k_codes=k_codes, k_scale=k_scale, k_mean=k_mean)
+    ws = _workspace(workspace)
+    _same_device(q, k, q_codes, q_scale, k_codes, k_scale, k_mean, workspace)
     qi, ki = bf16_in(q), bf16_in(k)
     st = lib().sage_quantize_qk(ctypes.byref(qi), ctypes.byref(ki), B, N, H, D, _ptr(q_codes), _ptr(q_scale),
-                                _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(stream))
+                                _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(workspace), ws, _stream(stream))
     _check(st, "sage_quantize_qk")
 
 
 def sage_quantize_v(v, v_codes, v_scale, workspace, stream=None) -> None:
     B, N, H, D = _shape(v)
+    _views((B, N, H, D), v=v)
+    _codes(B, N, H, D, v_codes=v_codes, v_scale=v_scale)
+    ws = _workspace(workspace)
+    _same_device(v, v_codes, v_scale, workspace)
     vi = bf16_in(v)
-    st = lib().sage_quantize_v(ctypes.byref(vi), B, N, H, D, _ptr(v_codes), _ptr(v_scale), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream))
+    st = lib().sage_quantize_v(ctypes.byref(vi), B, N, H, D, _ptr(v_codes), _ptr(v_scale), _ptr(workspace), ws,
+                               _stream(stream))
     _check(st, "sage_quantize_v")
 
 
@@ -157,20 +217,31 @@ def sage_qkv_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
 def sage_quantize_qkv(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
                       stream=None) -> None:
     B, N, H, D = _shape(q)
+    _views((B, N, H, D), q=q, k=k, v=v)
+    _codes(B, N, H, D, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale)
+    ws = _workspace(workspace)
+    _same_device(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, workspace)
     qi, ki, vi = bf16_in(q), bf16_in(k), bf16_in(v)
     st = lib().sage_quantize_qkv(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D, _ptr(q_codes),
                                  _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(v_codes),
-                                 _ptr(v_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(stream))
+                                 _ptr(v_scale), _ptr(workspace), ws, _stream(stream))
     _check(st, "sage_quantize_qkv")
+
+
+def _norm_rope_params(N: int, D: int, gamma_q, gamma_k, rope) -> None:
+    _need("gamma_q", gamma_q, torch.float32, D)
+    _need("gamma_k", gamma_k, torch.float32, D)
+    _need("rope", rope, torch.float32, N * D)
+    if tuple(rope.shape) != (N, D // 2, 2):
+        raise ValueError("rope: shape %s, expected %s" % (tuple(rope.shape), (N, D // 2, 2)))
 
 
 def sage_qk_norm_rope(q, k, gamma_q, gamma_k, rope, eps: float, stream=None) -> None:
     """RMSNorm + RoPE of the Q and K views, in place."""
     B, N, H, D = _shape(q)
-    assert tuple(k.shape) == (B, N, H, D) and tuple(rope.shape) == (N, D // 2, 2)
-    assert gamma_q.dtype == gamma_k.dtype == rope.dtype == torch.float32
-    assert gamma_q.is_contiguous() and gamma_k.is_contiguous() and rope.is_contiguous()
+    _views((B, N, H, D), q=q, k=k)
+    _norm_rope_params(N, D, gamma_q, gamma_k, rope)
+    _same_device(q, k, gamma_q, gamma_k, rope)
     qo, ko = bf16_out(q), bf16_out(k)
     st = lib().sage_qk_norm_rope(ctypes.byref(qo), ctypes.byref(ko), B, N, H, D, _ptr(gamma_q), _ptr(gamma_k),
                                  _ptr(rope), float(eps), _stream(stream))
@@ -180,19 +251,25 @@ def sage_qk_norm_rope(q, k, gamma_q, gamma_k, rope, eps: float, stream=None) -> 
 def sage_quantize_qkv_rope(q, k, v, gamma_q, gamma_k, rope, eps: float, q_codes, q_scale, k_codes, k_scale, k_mean,
                            v_codes, v_scale, workspace, stream=None) -> None:
     B, N, H, D = _shape(q)
-    assert tuple(rope.shape) == (N, D // 2, 2)
-    assert gamma_q.dtype == gamma_k.dtype == rope.dtype == torch.float32
-    assert gamma_q.is_contiguous() and gamma_k.is_contiguous() and rope.is_contiguous()
+    _views((B, N, H, D), q=q, k=k, v=v)
+    _norm_rope_params(N, D, gamma_q, gamma_k, rope)
+    _codes(B, N, H, D, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale)
+    ws = _workspace(workspace)
+    _same_device(q, k, v, gamma_q, gamma_k, rope, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale,
+                 workspace)
     qi, ki, vi = bf16_in(q), bf16_in(k), bf16_in(v)
     st = lib().sage_quantize_qkv_rope(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D, _ptr(gamma_q),
                                       _ptr(gamma_k), _ptr(rope), float(eps), _ptr(q_codes), _ptr(q_scale),
                                       _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(v_codes), _ptr(v_scale),
-                                      _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+                                      _ptr(workspace), ws, _stream(stream))
     _check(st, "sage_quantize_qkv_rope")
 
 
 def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, out, sm_scale=None, stream=None) -> None:
     B, N, H, D = _shape(out)
+    _views((B, N, H, D), out=out)
+    _codes(B, N, H, D, q_codes, q_scale, k_codes, k_scale, None, v_codes, v_scale)
+    _same_device(out, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     o = bf16_out(out)
@@ -203,6 +280,8 @@ def sage_attn_fwd(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, out, sm_
 
 def sage_attn_fwd_bf16(q, k, v, out, sm_scale=None, stream=None) -> None:
     B, N, H, D = _shape(q)
+    _views((B, N, H, D), q=q, k=k, v=v, out=out)
+    _same_device(q, k, v, out)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     qi, ki, vi, o = bf16_in(q), bf16_in(k), bf16_in(v), bf16_out(out)
@@ -213,6 +292,9 @@ def sage_attn_fwd_bf16(q, k, v, out, sm_scale=None, stream=None) -> None:
 
 def sage_attn_fwd_int8qk(q_codes, q_scale, k_codes, k_scale, v, out, sm_scale=None, stream=None) -> None:
     B, N, H, D = _shape(out)
+    _views((B, N, H, D), v=v, out=out)
+    _codes(B, N, H, D, q_codes, q_scale, k_codes, k_scale)
+    _same_device(v, out, q_codes, q_scale, k_codes, k_scale)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
     vi, o = bf16_in(v), bf16_out(out)
@@ -234,16 +316,29 @@ def mx_out(B: int, N: int, H: int, fmt: int, device="cuda", D: int = HEAD_DIM):
 
 
 def _mx_shape(codes, scales, fmt):
-    if not (codes.is_contiguous() and scales.is_contiguous()):
-        raise ValueError("MX codes and scales are contiguous token-major buffers")
+    """(B, N, H) of token-major MX buffers: codes [B, N, H*D] (E4M3) or
+    [B, N, H*D/2] (E2M1), scales [B, N, H*D/32], uint8, contiguous, on the GPU."""
+    if fmt not in (MX_E4M3, MX_E2M1):
+        raise ValueError("unknown MX format %r" % (fmt,))
+    for name, t in (("codes", codes), ("scales", scales)):
+        _on_gpu(name, t)
+        if t.dtype != torch.uint8 or t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("MX %s: a contiguous uint8 [B, N, *] token-major buffer" % name)
     B, N, per = codes.shape
+    if tuple(scales.shape[:2]) != (B, N) or (scales.shape[2] * 32) % HEAD_DIM:
+        raise ValueError("MX scales: shape %s does not match codes %s" % (tuple(scales.shape), tuple(codes.shape)))
     H = scales.shape[2] * 32 // HEAD_DIM
-    assert per == (H * HEAD_DIM if fmt == MX_E4M3 else H * HEAD_DIM // 2)
+    if per != (H * HEAD_DIM if fmt == MX_E4M3 else H * HEAD_DIM // 2):
+        raise ValueError("MX codes: shape %s does not match scales %s" % (tuple(codes.shape), tuple(scales.shape)))
     return B, N, H
 
 
 def sage_mx_quantize(x, fmt: int, codes, scales, stream=None) -> None:
     B, N, H, D = _shape(x)
+    _views((B, N, H, D), x=x)
+    if _mx_shape(codes, scales, fmt) != (B, N, H):
+        raise ValueError("MX buffers do not match x of shape %s" % ((B, N, H, D),))
+    _same_device(x, codes, scales)
     xi = bf16_in(x)
     st = lib().sage_mx_quantize(ctypes.byref(xi), B, N, H, D, int(fmt), _ptr(codes), _ptr(scales), _stream(stream))
     _check(st, "sage_mx_quantize")
@@ -252,6 +347,8 @@ def sage_mx_quantize(x, fmt: int, codes, scales, stream=None) -> None:
 def sage_attn_fwd_mx(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, fmt: int, codes, scales, sm_scale=None,
                      stream=None) -> None:
     B, N, H = _mx_shape(codes, scales, fmt)
+    _codes(B, N, H, HEAD_DIM, q_codes, q_scale, k_codes, k_scale, None, v_codes, v_scale)
+    _same_device(codes, scales, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale)
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     st = lib().sage_attn_fwd_mx(_ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(v_codes),
