@@ -210,3 +210,15 @@ def test_quantize_qkv_rope_validation():
     assert call(ptrs=(A + 8, A, A, A, A, A, A)) == ALIGN
     assert call(eps=float("inf")) == VALUE
     assert call(w=wsb - 8) == WORKSPACE
+
+
+@pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++11")])
+def test_header_is_plain_c_and_cxx(tmp_path, lang, std):
+    # the public header needs nothing beyond the C standard headers it includes
+    import subprocess
+    src = tmp_path / ("use." + ("c" if lang == "c" else "cpp"))
+    src.write_text('#include "sage_mi355x.h"\nint main(void) { return sage_npad(1) == 256 ? 0 : 1; }\n')
+    cc = "gcc" if lang == "c" else "g++"
+    r = subprocess.run([cc, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-fsyntax-only",
+                        "-I", os.path.dirname(HEADER), str(src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
