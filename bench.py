@@ -482,6 +482,35 @@ def main():
              "note": "per-GPU share of an 8-way head split, measured on one GPU; no multi-GPU run"}
     del sbuf
 
+    # the two-sequence stress workload: B=2, x10 outlier channels in Q and K,
+    # Student-t V (twice the block-24 work per call)
+    t0 = time.perf_counter()
+    sc = inputs.config("stress")
+    st_gen = time.perf_counter() - t0
+    sgc = sc.to(dev)
+    del sc
+    tbuf = sage.Buffers(2, N, H, device=dev)
+    tout = sage.token_major_out(2, N, H, device=dev)
+    et = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.bf16_calls)]
+    sage.forward(sgc.q, sgc.k, sgc.v, tout, tbuf, sm, stream)
+    for e in et:
+        e[0].record(stream)
+        sage.quantize_qkv(sgc.q, sgc.k, sgc.v, tbuf, stream)
+        e[1].record(stream)
+        sage.sage_attn_fwd(tbuf.q_codes, tbuf.q_scale, tbuf.k_codes, tbuf.k_scale, tbuf.v_codes, tbuf.v_scale,
+                           tout, sm, stream)
+        e[2].record(stream)
+    stream.synchronize()
+    t_q = [e[0].elapsed_time(e[1]) for e in et]
+    t_a = [e[1].elapsed_time(e[2]) for e in et]
+    f2, qb2 = attn_flops(b=2), quant_bytes(b=2)
+    stress = {"B": 2, "qkv_quantize_ms": stats_ms(t_q),
+              "qkv_quantize_GBps": (qb2["qk_quantize"] + qb2["v_quantize"]) / (statistics.fmean(t_q) * 1e-3) / 1e9,
+              "attn_fwd_ms": stats_ms(t_a), "attn_tflops": f2 / (statistics.fmean(t_a) * 1e-3) / 1e12,
+              "step_tflops": f2 / ((statistics.fmean(t_q) + statistics.fmean(t_a)) * 1e-3) / 1e12,
+              "input_generation_s": st_gen}
+    del sgc, tbuf, tout
+
     line = {
         "metric": METRIC,
         "value": value,
@@ -528,6 +557,7 @@ def main():
         "rope_path": rope,
         "mx_path": mx,
         "head_shard": shard,
+        "stress_path": stress,
         "pages_context": {"gb10_attention_forward_p50_ms": 238.995, "gb10_total_excluding_layout_ms": 258.613,
                           "note": "NVIDIA GB10 on real activations; context only"},
         "input_generation_s": gen_s,
