@@ -23,6 +23,12 @@ Prints ONE JSON line.  Besides the contract keys it carries:
                    MX quantiser (sage_mx_quantize) on the bf16 output.
   cpu_baseline  -- the CPU oracle (quantisers in full + step-by-step quantised
                    attention on sampled rows, extrapolated), on the host cores.
+  parity        -- the timed output at those sampled rows against the oracle's
+                   result (rounded to bf16): whole-set rel-L2 and the largest
+                   row error against the typical row norm (plus each row's
+                   error against its own norm, and the worst rows); the run
+                   exits non-zero above the gates.
+  output_sha256 -- digest of the timed output's bytes.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--copy-calibration]
 """
@@ -46,6 +52,11 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PEAK_INT8QK_TFLOPS = 1.0 / (0.5 / PEAK_I8F8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)   # INT8 QK^T + BF16 P.V
 B, N, H, D = 1, 37810, 56, 128
+PARITY_GATE = 1e-3        # timed output vs the quantised oracle, whole sampled set
+PARITY_ROW_GATE = 3e-2    # ... and each sampled row's error against the typical (RMS) row norm: one wrong
+                          # element of a row gives ~0.09; one E4M3 rounding of a large p at a midpoint,
+                          # taken the other way in fp32 than in fp64, up to ~0.015
+
 
 
 def attn_flops(b=B, n=N, h=H, d=D) -> float:
@@ -149,11 +160,12 @@ def cpu_baseline(case, rows_per_head=512, heads=None):
     rows = inputs.sample_rows(case.B, case.H, case.N, count=rows_per_head, tail=64)[:, :heads]
     sub = lambda a: np.ascontiguousarray(a[:, :heads])
     t0 = time.perf_counter()
-    oracle.attn_method(sub(qc), sub(qs), sub(kc), sub(ks), sub(vc), sub(vs), 1.0 / math.sqrt(D), rows)
+    meth = oracle.attn_method(sub(qc), sub(qs), sub(kc), sub(ks), sub(vc), sub(vs), 1.0 / math.sqrt(D), rows)
     t_attn = time.perf_counter() - t0
     scale = (case.N * case.H) / (rows_per_head * heads)
     t_call = t_quant + t_attn * scale
-    return {
+    extras = {"rows": rows, "method": meth, "codes": (qc, qs, kc, ks), "heads": heads}
+    return extras, {
         "value": attn_flops(case.B, case.N, case.H, case.D) / t_call / 1e12,
         "unit": "TFLOP/s",
         "ms_per_call_extrapolated": t_call * 1e3,
@@ -167,6 +179,77 @@ def cpu_baseline(case, rows_per_head=512, heads=None):
                    "to %d rows x %d heads" % (t_quant, rows_per_head, heads, case.N, t_attn, scale, case.N,
                                               case.H)),
     }
+
+
+def parity_vs_method(out, rows, meth):
+    """The timed bf16 output [B, N, H*D] (token-major, on the GPU) at the oracle's sampled rows [B, H', R]
+    against the step-by-step quantised oracle's result there [B, H', R, D], rounded to bf16 as the kernel
+    stores it: whole-set rel-L2 and the largest per-row rel-L2."""
+    import numpy as np
+    import torch
+
+    Bq, Hq, R = rows.shape
+    o = out.view(out.shape[0], out.shape[1], -1, D)[:, :, :Hq]            # [B, N, H', D]
+    idx = torch.from_numpy(np.ascontiguousarray(rows.transpose(0, 2, 1))).long().to(out.device)   # [B, R, H']
+    got = torch.gather(o, 1, idx[..., None].expand(Bq, R, Hq, D)).float().cpu().numpy()
+    got = got.transpose(0, 2, 1, 3).astype(np.float64)                      # [B, H', R, D]
+    ref = torch.from_numpy(meth).float().to(torch.bfloat16).double().numpy()
+    err = np.sqrt(((got - ref) ** 2).sum(-1))
+    nrm = np.sqrt((ref ** 2).sum(-1))
+    typical = float(np.sqrt((nrm ** 2).mean()))          # RMS row norm
+    own = err / np.maximum(nrm, 1e-300)
+    worst = np.argsort(own.ravel())[::-1][:5]
+    return {"rel_l2_vs_method": float(np.sqrt((err ** 2).sum() / (nrm ** 2).sum())),
+            "max_row_err_vs_typical_row": float(err.max() / typical),
+            "max_row_rel_l2": float(own.max()),
+            "worst_rows": [{"b": int(i // (Hq * R)), "h": int(i // R % Hq), "row": int(rows.ravel()[i]),
+                            "rel_l2": float(own.ravel()[i]), "norm_vs_typical": float(nrm.ravel()[i] / typical)}
+                           for i in worst],
+            "rows": int(Bq * Hq * R), "reference": "step-by-step quantised oracle, rounded to bf16",
+            "gate": {"rel_l2_vs_method": PARITY_GATE, "max_row_err_vs_typical_row": PARITY_ROW_GATE}}
+
+
+def rescale_fraction(codes, N, H, waves_per_head=4, head_step=7):
+    """Share of the attention kernel's tiles (after the first) in which some row maximum of a 32-query wave
+    moves, so the wave rescales its 64 output accumulators: taken on the workload's own INT8 codes for a
+    sample of waves (waves_per_head evenly spaced 32-query blocks of every head_step-th head), with the
+    kernel's fp32 scale products."""
+    import numpy as np
+
+    qc, qs, kc, ks = codes
+    cb = np.float32(1.0 / math.sqrt(D)) * np.float32(1.4426950408889634)
+    T = -(-N // 64)
+    fired = total = 0
+    for h in range(0, H, head_step):
+        K = kc[0, h, :N].astype(np.float64)
+        for w in range(waves_per_head):
+            q0 = (w * (N // waves_per_head)) // 32 * 32
+            Q = qc[0, h, q0:q0 + 32].astype(np.float64)
+            S = Q @ K.T                                              # exact integer scores [32, N]
+            pad = T * 64 - N
+            S = np.concatenate([S, np.full((S.shape[0], pad), -np.inf)], axis=1).reshape(S.shape[0], T, 64)
+            amax = S.max(axis=2).astype(np.float32)                  # [32, T]
+            cq = np.float32(qs[0, h, q0 // 32]) * cb
+            c2 = (cq * ks[0, h, :T].astype(np.float32)).astype(np.float32)
+            m = np.full(Q.shape[0], -np.inf, np.float32)
+            for t in range(T):
+                mn = np.maximum(m, c2[t] * amax[:, t])
+                if t > 0:
+                    fired += bool((mn != m).any())
+                    total += 1
+                m = mn
+    return fired / max(total, 1)
+
+
+def valu_floor(rescale_frac):
+    """Issue floor of the attention's per-tile instruction stream at two waves per SIMD, from the committed
+    tile-replay measurement (profiles/valu_rates.json): SIMD cycles per wave-tile."""
+    path = os.path.join(ROOT, "profiles", "valu_rates.json")
+    if not os.path.exists(path):
+        return None
+    rep = json.load(open(path))["rates"]["tile_replay"]
+    t0, t64 = rep["rescale_0"]["2"]["cyc_per_tile"], rep["rescale_64"]["2"]["cyc_per_tile"]
+    return t0 + rescale_frac * (t64 - t0)
 
 
 def stats_ms(xs):
@@ -304,6 +387,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
 
+    out_sha = hashlib.sha256(out.view(torch.int16).cpu().numpy().tobytes()).hexdigest()
     qkv_ms = [e[0].elapsed_time(e[1]) for e in evs]
     at_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
@@ -562,9 +646,32 @@ def main():
                           "note": "NVIDIA GB10 on real activations; context only"},
         "input_generation_s": gen_s,
     }
+    line["output_sha256"] = out_sha
+    ok = True
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(case)
+        extras, line["cpu_baseline"] = cpu_baseline(case)
+        par = parity_vs_method(out, extras["rows"], extras["method"])
+        line["parity"] = par
+        ok = par["rel_l2_vs_method"] <= PARITY_GATE and par["max_row_err_vs_typical_row"] <= PARITY_ROW_GATE
+        # VALU roofline of the attention kernel: the issue floor of its instruction stream (tile replay) at
+        # the workload's share of rescaling tiles, over the measured kernel time at the measured clock
+        frac = rescale_fraction(extras["codes"], N, H)
+        floor = valu_floor(frac)
+        wave_tiles_per_simd = (-(-N // 128)) * 4 * H * B * (-(-N // 64)) / 1024.0
+        line["roofline"]["rescale_fraction"] = frac
+        line["roofline"]["valu_floor_cycles_per_wave_tile"] = floor
+        if floor is not None and sclk:
+            t_floor = floor * wave_tiles_per_simd / (sclk * 1e6)
+            line["roofline"]["valu_floor_ms_at_measured_sclk"] = t_floor * 1e3
+            line["roofline"]["valu_frac"] = t_floor / (attn_mean * 1e-3)
+        else:
+            line["roofline"]["valu_frac"] = None
+    else:
+        line["parity"] = None
     print(json.dumps(line), flush=True)
+    if not ok:
+        print("bench.py: the timed output is not within the parity gate of the quantised oracle", file=sys.stderr)
+        sys.exit(1)
 
 
 if __name__ == "__main__":

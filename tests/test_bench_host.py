@@ -36,3 +36,65 @@ def test_stats_percentiles():
     s = bench.stats_ms([5.0, 1.0, 3.0, 2.0, 4.0])
     assert s["min"] == 1.0 and s["max"] == 5.0 and s["p50"] == 3.0 and s["mean"] == 3.0 and s["count"] == 5
     assert s["p90"] == 5.0 and s["p99"] == 5.0
+
+
+def _tiny_oracle():
+    import oracle
+    from quantized_softmax_attention_amd import inputs
+    from tests.helpers import oracle_view
+
+    case = inputs.config("tiny")
+    q, k, v = (oracle_view(t) for t in (case.q, case.k, case.v))
+    qc, qs = oracle.quant_q(q, 32)
+    kc, ks = oracle.quant_k(k, oracle.kmean(k), 64)
+    vc, vs = oracle.quant_v(v)
+    return case, (qc, qs, kc, ks, vc, vs)
+
+
+def test_parity_vs_method_is_exact_on_the_method_and_local():
+    """The bench's parity check: zero when the 'timed output' is the oracle's own bf16 result at the
+    sampled rows, and one wrong element in one row trips the per-row gate while the whole-set figure
+    would not."""
+    import math
+
+    import numpy as np
+    import oracle
+    import torch
+    from quantized_softmax_attention_amd import inputs
+
+    case, (qc, qs, kc, ks, vc, vs) = _tiny_oracle()
+    B, N, H, D = case.B, case.N, case.H, case.D
+    rows = inputs.sample_rows(B, H, N, count=64, tail=16)
+    meth = oracle.attn_method(qc, qs, kc, ks, vc, vs, 1.0 / math.sqrt(D), rows)
+    full = oracle.attn_method(qc, qs, kc, ks, vc, vs, 1.0 / math.sqrt(D))          # [B, H, N, D]
+    out = torch.from_numpy(full.transpose(0, 2, 1, 3).reshape(B, N, H * D)).float().to(torch.bfloat16)
+    p = bench.parity_vs_method(out, rows, meth)
+    assert p["rel_l2_vs_method"] == 0.0 and p["max_row_rel_l2"] == 0.0 and p["rows"] == B * H * 64
+    assert p["max_row_err_vs_typical_row"] == 0.0
+    r = int(rows[0, 1, 5])
+    bad = out.clone()
+    bad[0, r, 1 * D + 17] = -bad[0, r, 1 * D + 17] * 3 + 1
+    p = bench.parity_vs_method(bad, rows, meth)
+    assert p["max_row_err_vs_typical_row"] > 3 * bench.PARITY_ROW_GATE
+    assert p["rel_l2_vs_method"] < p["max_row_err_vs_typical_row"]
+    assert p["worst_rows"][0]["row"] == r and p["worst_rows"][0]["h"] == 1
+
+
+def test_rescale_fraction_counts_moved_maxima():
+    """The share of tiles where a 32-query wave rescales: every tile after the first for a one-tile-per-step
+    workload whose scores grow monotonically with the key index, none when they shrink."""
+    import numpy as np
+
+    N, H = 256, 1
+    kc = np.zeros((1, H, N, 128), np.int8)
+    qc = np.zeros((1, H, N, 128), np.int8)
+    qc[..., 0] = 1
+    kc[0, 0, :, 0] = (np.arange(N) // 2).astype(np.int8)        # scores rise with the key index
+    qs = np.ones((1, H, N // 32), np.float32)
+    ks = np.ones((1, H, N // 64), np.float32)
+    assert bench.rescale_fraction((qc, qs, kc, ks), N, H, waves_per_head=2, head_step=1) == 1.0
+    kc[0, 0, :, 0] = (127 - np.arange(N) // 2).astype(np.int8)  # falling: the first tile holds the maximum
+    assert bench.rescale_fraction((qc, qs, kc, ks), N, H, waves_per_head=2, head_step=1) == 0.0
+    _, (qc, qs, kc, ks, _, _) = _tiny_oracle()
+    f = bench.rescale_fraction((qc, qs, kc, ks), 256, 2, waves_per_head=4, head_step=1)
+    assert 0.0 < f <= 1.0

@@ -1,7 +1,8 @@
 """Quantised attention forward on the GPU through the C ABI, against the oracle.
 
 Gate (reading of the tolerance for an approximate method): the GPU output is
-within rel-L2 1e-3 of the step-by-step quantised-method oracle with the
+within rel-L2 1e-3 of the step-by-step quantised-method oracle (and every
+compared row within 2e-2 of the typical row norm, tests/gpu_common.py) with the
 output's own bf16 rounding applied (the output is defined as the bf16 rounding
 of the fp32 result; that rounding alone is ~1.6e-3 rms relative, so it is taken
 on both sides), and within floor + 1e-3 of the exact fp64 oracle, where floor
@@ -33,11 +34,10 @@ def _rows(case, spec):
 def _gate(got, ref: G.OracleRef, rows, label):
     meth = ref.method(rows)
     exact = ref.exact(rows)
-    e_m = G.rel_l2(got, G.bf16_round(meth))
+    e_m = G.gate(got, G.bf16_round(meth), 1e-3, label + " vs method")
     e_x = G.rel_l2(got, exact)
     floor = G.rel_l2(meth, exact)
-    print("%s: rel-L2 vs method %.3e, vs exact %.3e, method floor %.3e" % (label, e_m, e_x, floor), flush=True)
-    assert e_m <= 1e-3, (label, e_m)
+    print("%s: rel-L2 vs exact %.3e, method floor %.3e" % (label, e_x, floor), flush=True)
     assert e_x <= floor + 1e-3, (label, e_x, floor)
     return e_m, e_x, floor
 
@@ -61,7 +61,7 @@ def test_attn_parity_ragged(N):
     rows = _rows(case, None)
     got = G.out_rows(out, rows)
     meth = ref.method(rows)
-    assert G.rel_l2(got, G.bf16_round(meth)) <= 1e-3
+    G.gate(got, G.bf16_round(meth), 1e-3, "ragged N=%d" % N)
     if N == 1:   # one key: the output is the dequantised v_0 (bf16-rounded)
         vc, vs = ref.vq
         from oracle import e4m3_decode

@@ -35,13 +35,16 @@ def _run(path, case):
 
 
 def _gate(path, ref, out, rows):
-    """rel-L2 of the sampled rows against the path's own oracle, and its bound."""
+    """rel-L2 of the sampled rows against the path's own oracle, and its bound (every row is also held to
+    the per-row bound of gpu_common.gate)."""
     got = G.out_rows(out, rows)
     if path == "i8f8":
-        return G.rel_l2(got, G.bf16_round(ref.method(rows))), 1e-3
-    if path == "int8qk":
-        return G.rel_l2(got, G.bf16_round(ref.int8qk(rows))), 1e-3
-    return G.rel_l2(got, ref.exact(rows)), 5e-3
+        want, bound = G.bf16_round(ref.method(rows)), 1e-3
+    elif path == "int8qk":
+        want, bound = G.bf16_round(ref.int8qk(rows)), 1e-3
+    else:
+        want, bound = ref.exact(rows), 5e-3
+    return G.gate(got, want, bound, path), bound
 
 
 def _v_used(path, ref):
@@ -69,9 +72,8 @@ def test_long_sequence_parity():
     rows = inputs.sample_rows(1, 1, N, count=96, tail=32)
     got = G.out_rows(out, rows)
     meth, exact = ref.method(rows), ref.exact(rows)
-    e_m, floor = G.rel_l2(got, G.bf16_round(meth)), G.rel_l2(meth, exact)
-    print("N=%d: rel-L2 vs method %.3e, method floor %.3e" % (N, e_m, floor), flush=True)
-    assert e_m <= 1e-3
+    e_m, floor = G.gate(got, G.bf16_round(meth), 1e-3, "N=%d vs method" % N), G.rel_l2(meth, exact)
+    print("N=%d: method floor %.3e" % (N, floor), flush=True)
     assert G.rel_l2(got, exact) <= floor + 1e-3
 
 

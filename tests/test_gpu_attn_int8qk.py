@@ -38,11 +38,10 @@ def test_int8qk_parity_workloads(name):
     got = G.out_rows(out, rows)
     meth = ref.int8qk(rows)
     exact = ref.exact(rows)
-    e_m = G.rel_l2(got, G.bf16_round(meth))
+    G.gate(got, G.bf16_round(meth), 1e-3, "%s vs int8qk oracle" % name)
     e_x = G.rel_l2(got, exact)
     floor = G.rel_l2(meth, exact)
-    print("%s: rel-L2 vs int8qk oracle %.3e, vs exact %.3e, oracle floor %.3e" % (name, e_m, e_x, floor), flush=True)
-    assert e_m <= 1e-3
+    print("%s: rel-L2 vs exact %.3e, oracle floor %.3e" % (name, e_x, floor), flush=True)
     if name == "stress":
         assert e_x <= floor + 1e-3
     else:
@@ -57,7 +56,7 @@ def test_int8qk_parity_ragged(N):
     out, _ = G.run_attn_int8qk(G.gpu_case(case))
     rows = _rows(case, (256, 64) if N > 1000 else None)
     got = G.out_rows(out, rows)
-    assert G.rel_l2(got, G.bf16_round(ref.int8qk(rows))) <= 1e-3
+    G.gate(got, G.bf16_round(ref.int8qk(rows)), 1e-3, "int8qk ragged N=%d" % N)
     if N == 1:   # one key: the output is v_0 itself
         assert torch.equal(out.cpu()[:, 0], case.v[:, 0])
 
