@@ -34,6 +34,8 @@
  *     `stream`: the library never synchronises, allocates, frees or caches
  *     device memory, holds no mutable global state and is re-entrant.  The
  *     caller owns every buffer and keeps it alive until the work completes.
+ *     The one exception is sage_quantize_qkv_noalloc, whose scratch is a device
+ *     array of the library's own, shared by all its calls on a GPU.
  *   - bf16 inputs are [B, N, H, D] views with unit d-stride and element strides
  *     (stride_b, stride_n, stride_h).  Contiguous HND, contiguous NHD and the
  *     strided views of a packed [B, N, 3*H*D] projection buffer are all such views.
@@ -154,6 +156,27 @@ int sage_quantize_qkv(const sage_bf16_in *q, const sage_bf16_in *k, const sage_b
                       int D, int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale,
                       float *k_mean, uint8_t *v_codes, float *v_scale, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/* sage_quantize_qkv for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same three kernels and the same outputs, bit for bit, with no workspace
+ * argument.  Their scratch (sage_qkv_workspace_bytes(B, N, H, D) bytes) lives in
+ * a device array owned by the library, of sage_qkv_noalloc_max_bytes() = 64 MiB:
+ * each GPU it is called on holds its own copy from the first call until the
+ * process ends.  The call allocates and frees nothing; the first call on a
+ * device looks the array's address up (hipGetSymbolAddress) with that device
+ * current.  Every call on one GPU shares its copy and leaves its own contents
+ * there, so calls that overlap on one GPU (different streams, or host threads)
+ * race: serialise them.  Each call writes every scratch entry it reads, so
+ * nothing has to be cleared between calls.  Sizes whose scratch exceeds 64 MiB
+ * (sage_qkv_workspace_bytes > sage_qkv_noalloc_max_bytes(), i.e. about
+ * B * H * ceil(N/64) > 43690; one block-24 sequence, N = 37810, H = 56, needs
+ * 50.9 MB, two do not fit) return SAGE_ERR_WORKSPACE before anything is
+ * enqueued.  Other arguments and errors as sage_quantize_qkv. */
+size_t sage_qkv_noalloc_max_bytes(void);
+int sage_quantize_qkv_noalloc(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N,
+                              int H, int D, int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale,
+                              float *k_mean, uint8_t *v_codes, float *v_scale, void *stream);
 
 /* The step before quantisation: RMSNorm and rotary position embedding of Q and K
  * in place on their strided views (strided page, dataflow.qk_transform; profile

@@ -3,6 +3,7 @@
 // stream.  No allocation, no synchronisation, no global mutable state.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sage_common.h"
 #include "sage_norm_rope.h"
@@ -190,6 +191,66 @@ int sage_quantize_qkv(const sage_bf16_in *q, const sage_bf16_in *k, const sage_b
     if (workspace_bytes < sage_qkv_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
     return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, nullptr, q_codes,
                                                 q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+// ---- sage_quantize_qkv_noalloc: sage_quantize_qkv with library-owned scratch
+}  // extern "C"
+
+namespace {
+
+// The scratch of sage_quantize_qkv_noalloc (the K-mean chunk partials, the V
+// channel maxima and their reduction: sage_qkv_workspace_bytes of it per call).
+// A device global: every GPU the library runs on holds its own copy from the
+// first use until the process ends, and every call on that GPU shares it.  In
+// host code `scratch` only names the symbol; its device address on the current
+// device comes from hipGetSymbolAddress (noalloc_scratch below).
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];   // per device ordinal: the address of its copy, set on first use
+
+// This device's copy of `scratch`, looked up once per device (with it current).
+hipError_t noalloc_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sage_qkv_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+int sage_quantize_qkv_noalloc(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N,
+                              int H, int D, int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale,
+                              float *k_mean, uint8_t *v_codes, float *v_scale, void *stream) {
+    int st;
+    if ((st = check_in(q)) || (st = check_in(k)) || (st = check_in(v))) return st;
+    if (!q_codes || !q_scale || !k_codes || !k_scale || !k_mean || !v_codes || !v_scale) return SAGE_ERR_NULL;
+    if ((st = check_shape(B, N, H, D))) return st;
+    if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scale, 4) ||
+        !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4))
+        return SAGE_ERR_ALIGN;
+    if (sage_qkv_workspace_bytes(B, N, H, D) > kNoallocScratchBytes) return SAGE_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (noalloc_scratch(&ws) != hipSuccess) return SAGE_ERR_HIP;
+    return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, nullptr, q_codes,
+                                                q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, ws,
                                                 static_cast<hipStream_t>(stream)));
 }
 

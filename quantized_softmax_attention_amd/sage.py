@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.sage_v_workspace_bytes.argtypes, L.sage_v_workspace_bytes.restype = [i, i, i, i], sz
         L.sage_qkv_workspace_bytes.argtypes, L.sage_qkv_workspace_bytes.restype = [i, i, i, i], sz
         L.sage_quantize_qkv.argtypes = [pin, pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.sage_quantize_qkv_noalloc.argtypes = [pin, pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.sage_qkv_noalloc_max_bytes.argtypes, L.sage_qkv_noalloc_max_bytes.restype = [], sz
         L.sage_quantize_qk.argtypes = [pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_v.argtypes = [pin, i, i, i, i, vp, vp, vp, sz, vp]
         L.sage_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, pout, vp]
@@ -73,7 +75,8 @@ def lib() -> ctypes.CDLL:
                                              vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sage_mx_quantize.argtypes = [pin, i, i, i, i, i, vp, vp, vp]
         L.sage_attn_fwd_mx.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, vp]
-        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_quantize_qkv", "sage_attn_fwd", "sage_attn_fwd_bf16",
+        for fn in ("sage_quantize_qk", "sage_quantize_v", "sage_quantize_qkv", "sage_quantize_qkv_noalloc",
+                   "sage_attn_fwd", "sage_attn_fwd_bf16",
                    "sage_attn_fwd_int8qk", "sage_mx_quantize", "sage_attn_fwd_mx", "sage_qk_norm_rope",
                    "sage_quantize_qkv_rope"):
             getattr(L, fn).restype = i
@@ -226,6 +229,24 @@ def sage_quantize_qkv(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_cod
                                  _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(k_mean), _ptr(v_codes),
                                  _ptr(v_scale), _ptr(workspace), ws, _stream(stream))
     _check(st, "sage_quantize_qkv")
+
+
+def sage_qkv_noalloc_max_bytes() -> int:
+    return int(lib().sage_qkv_noalloc_max_bytes())
+
+
+def sage_quantize_qkv_noalloc(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale,
+                              stream=None) -> None:
+    """sage_quantize_qkv without a workspace: its scratch is the library's own device array (see the header)."""
+    B, N, H, D = _shape(q)
+    _views((B, N, H, D), q=q, k=k, v=v)
+    _codes(B, N, H, D, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale)
+    _same_device(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale)
+    qi, ki, vi = bf16_in(q), bf16_in(k), bf16_in(v)
+    st = lib().sage_quantize_qkv_noalloc(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), B, N, H, D,
+                                         _ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale), _ptr(k_mean),
+                                         _ptr(v_codes), _ptr(v_scale), _stream(stream))
+    _check(st, "sage_quantize_qkv_noalloc")
 
 
 def _norm_rope_params(N: int, D: int, gamma_q, gamma_k, rope) -> None:

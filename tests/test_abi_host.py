@@ -156,6 +156,25 @@ def test_quantize_qkv_validation():
     assert call(w=wsb - 8) == WORKSPACE
 
 
+def test_quantize_qkv_noalloc_validation():
+    """The allocation-free quantiser validates like sage_quantize_qkv and refuses sizes whose scratch
+    exceeds its fixed array, all before any HIP call."""
+    L = sage.lib()
+    assert sage.sage_qkv_noalloc_max_bytes() == 64 << 20
+    call = lambda q=None, ptrs=(A,) * 7, Bv=B, Nv=N, Hv=H, Dv=D: L.sage_quantize_qkv_noalloc(
+        ctypes.byref(q or view()), ctypes.byref(view(A + 2 * H * D)), ctypes.byref(view(A + 4 * H * D)), Bv, Nv, Hv,
+        Dv, *ptrs, None)
+    assert call(ptrs=(A, A, A, A, A, None, A)) == NULL
+    assert call(Dv=96) == SHAPE
+    assert call(ptrs=(A, A, A, A, A, A + 8, A)) == ALIGN
+    assert call(q=view(sn=-8)) == STRIDE
+    # two block-24 sequences need 101.7 MB of scratch, one fits (50.9 MB)
+    big = view(sb=37810 * 3 * 56 * D, sn=3 * 56 * D)
+    assert sage.sage_qkv_workspace_bytes(2, 37810, 56, D) > sage.sage_qkv_noalloc_max_bytes()
+    assert sage.sage_qkv_workspace_bytes(1, 37810, 56, D) <= sage.sage_qkv_noalloc_max_bytes()
+    assert call(q=big, Bv=2, Nv=37810, Hv=56) == WORKSPACE
+
+
 def test_mx_quantize_validation():
     L = sage.lib()
     call = lambda x=None, c=A, s=A, fmt=0, Dv=D: L.sage_mx_quantize(ctypes.byref(x or view()), B, N, H, Dv, fmt, c, s,
