@@ -44,8 +44,11 @@
  *     tokens; entries for tokens N..Npad-1 are written as zero.
  *   - Errors: arguments are validated on the host before anything is enqueued
  *     and a non-zero sage_status is returned (nothing is launched).  A failed
- *     launch returns SAGE_ERR_HIP.  There is no fallback path.  NaN or infinite
- *     inputs are outside the contract and are not checked.
+ *     launch returns SAGE_ERR_HIP: the status is that of the call's own kernel
+ *     launches (hipLaunchKernel's return values, the first failing one stops
+ *     the call); the thread's last-error state left by the caller's earlier HIP
+ *     calls is neither reported nor cleared.  There is no fallback path.  NaN
+ *     or infinite inputs are outside the contract and are not checked.
  */
 #ifndef SAGE_MI355X_H
 #define SAGE_MI355X_H

@@ -27,13 +27,21 @@ GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=o
              "-fno-fast-math", "-Wall", "-Wextra"]
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+# Opt-in sanitizer builds (the tests' sanitizer runs): libsage_oracle_<name>.so beside the normal one.
+SANITIZERS = {"ubsan": ["-fsanitize=undefined", "-fno-sanitize-recover=all", "-g"],
+              "asan": ["-fsanitize=address", "-fno-omit-frame-pointer", "-g"]}
+
+
+def build(force: bool = True, sanitize: str | None = None) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction); with sanitize="ubsan" or "asan" a
+    separately named library built under that sanitizer (load it by setting oracle._LIB to the path)."""
+    out = _LIB if sanitize is None else os.path.join(_HERE, "libsage_oracle_%s.so" % sanitize)
+    extra = [] if sanitize is None else SANITIZERS[sanitize]
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *GCC_FLAGS, *extra, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None

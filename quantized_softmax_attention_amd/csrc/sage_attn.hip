@@ -378,9 +378,9 @@ hipError_t launch_attn_fwd(const int8_t *qc, const float *qs, const int8_t *kc, 
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     const int nqwg = (N + kQWg - 1) / kQWg;
     const int64_t blocks = (int64_t)nqwg * H * B;
-    hipLaunchKernelGGL(attn_i8f8_kernel<-1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc, ks, vc,
+    LAUNCH_OR_RETURN(attn_i8f8_kernel<-1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc, ks, vc,
                        vs, N, H, Npad, sm_scale * kLog2E, out, nullptr, nullptr, nqwg);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_attn_fwd_mx(const int8_t *qc, const float *qs, const int8_t *kc, const float *ks, const uint8_t *vc,
@@ -391,12 +391,12 @@ hipError_t launch_attn_fwd_mx(const int8_t *qc, const float *qs, const int8_t *k
     const int64_t blocks = (int64_t)nqwg * H * B;
     const OutView none{nullptr, 0, 0, 0};
     if (fmt == kMxE4M3)
-        hipLaunchKernelGGL(attn_i8f8_kernel<kMxE4M3>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc,
+        LAUNCH_OR_RETURN(attn_i8f8_kernel<kMxE4M3>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc,
                            ks, vc, vs, N, H, Npad, sm_scale * kLog2E, none, codes, scales, nqwg);
     else
-        hipLaunchKernelGGL(attn_i8f8_kernel<kMxE2M1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc,
+        LAUNCH_OR_RETURN(attn_i8f8_kernel<kMxE2M1>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc,
                            ks, vc, vs, N, H, Npad, sm_scale * kLog2E, none, codes, scales, nqwg);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sage

@@ -240,9 +240,9 @@ hipError_t launch_attn_fwd_bf16(View q, View k, View v, int B, int N, int H, flo
                                 hipStream_t stream) {
     const int nqwg = (N + kQWg - 1) / kQWg;
     const int64_t blocks = (int64_t)nqwg * H * B;
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, k, v, N, H,
+    LAUNCH_OR_RETURN(attn_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, q, k, v, N, H,
                        sm_scale * kLog2E, out, nqwg);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sage

@@ -227,9 +227,9 @@ hipError_t launch_attn_fwd_int8qk(const int8_t *qc, const float *qs, const int8_
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     const int nqwg = (N + kQWg - 1) / kQWg;
     const int64_t blocks = (int64_t)nqwg * H * B;
-    hipLaunchKernelGGL(attn_int8qk_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc, ks, v, N,
+    LAUNCH_OR_RETURN(attn_int8qk_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, qc, qs, kc, ks, v, N,
                        H, Npad, sm_scale * kLog2E, out, nqwg);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sage

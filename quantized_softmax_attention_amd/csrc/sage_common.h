@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 #include "sage_mi355x.h"
 
 namespace sage {
@@ -103,5 +106,31 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t id, uint32_t n) {
     if (n % 8u) return id;
     return (id % 8u) * (n / 8u) + id / 8u;
 }
+
+// kernel<<<grid, block, shmem, stream>>>(args...) through hipLaunchKernel,
+// returning that launch's own status.  (hipGetLastError() after a launch would
+// also report, and clear, an error left by the caller's earlier HIP work.)  The
+// arguments are converted to the kernel's parameter types first, as a direct
+// launch converts them.
+template <typename... P, size_t... I>
+hipError_t launch_packed(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream,
+                         std::index_sequence<I...>, std::tuple<P...> &args) {
+    void *ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1] = {static_cast<void *>(&std::get<I>(args))...};
+    return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, shmem, stream);
+}
+
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t shmem, hipStream_t stream, A &&...args) {
+    static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+    std::tuple<P...> packed(std::forward<A>(args)...);
+    return launch_packed(kernel, grid, block, shmem, stream, std::index_sequence_for<P...>{}, packed);
+}
+
+// In a launcher returning hipError_t: launch, and return the status if it failed.
+#define LAUNCH_OR_RETURN(kernel, ...)                                   \
+    do {                                                                \
+        const hipError_t launch_status_ = ::sage::launch(kernel, __VA_ARGS__); \
+        if (launch_status_ != hipSuccess) return launch_status_;        \
+    } while (0)
 
 }  // namespace sage

@@ -60,10 +60,10 @@ hipError_t launch_mx_quantize(View x, int B, int N, int H, int fmt, uint8_t *cod
     const int64_t nblocks = (int64_t)B * N * H * (kD / kMxBlock);
     const dim3 grid((unsigned)((nblocks + 255) / 256));
     if (fmt == kMxE4M3)
-        hipLaunchKernelGGL(mx_quantize_kernel<kMxE4M3>, grid, dim3(256), 0, stream, x, N, H, nblocks, codes, scales);
+        LAUNCH_OR_RETURN(mx_quantize_kernel<kMxE4M3>, grid, dim3(256), 0, stream, x, N, H, nblocks, codes, scales);
     else
-        hipLaunchKernelGGL(mx_quantize_kernel<kMxE2M1>, grid, dim3(256), 0, stream, x, N, H, nblocks, codes, scales);
-    return hipGetLastError();
+        LAUNCH_OR_RETURN(mx_quantize_kernel<kMxE2M1>, grid, dim3(256), 0, stream, x, N, H, nblocks, codes, scales);
+    return hipSuccess;
 }
 
 }  // namespace sage

@@ -661,13 +661,13 @@ hipError_t launch_quantize_qk(View q, View k, int B, int N, int H, int8_t *qc, f
     const int nchunk = (N + kSumChunk - 1) / kSumChunk;
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     double *ws = static_cast<double *>(workspace);
-    hipLaunchKernelGGL(kmean_partial_kernel, dim3((nchunk + 15) / 16, H, B), dim3(256), 0, stream, k, N, H, nchunk,
+    LAUNCH_OR_RETURN(kmean_partial_kernel, dim3((nchunk + 15) / 16, H, B), dim3(256), 0, stream, k, N, H, nchunk,
                        ws);
-    hipLaunchKernelGGL((chunk_final_kernel<true, false>), final_grid(B, H), dim3(256), 0, stream, ws, nullptr, N, H,
+    LAUNCH_OR_RETURN((chunk_final_kernel<true, false>), final_grid(B, H), dim3(256), 0, stream, ws, nullptr, N, H,
                        nchunk, km, nullptr, nullptr);
-    hipLaunchKernelGGL(quant_qk_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, q, k, N, H,
+    LAUNCH_OR_RETURN(quant_qk_kernel, dim3((unsigned)(Npad / 64), H, B), dim3(256), 0, stream, q, k, N, H,
                        Npad, km, qc, qs, kc, ks);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs, void *workspace,
@@ -676,12 +676,12 @@ hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs
     const int64_t Npad = ((int64_t)N + kNAlign - 1) / kNAlign * kNAlign;
     float *part = static_cast<float *>(workspace);
     float *amax = part + (int64_t)nchunk * B * H * kD;
-    hipLaunchKernelGGL(v_amax_partial_kernel, dim3(nchunk, H, B), dim3(256), 0, stream, v, N, H, nchunk, part);
-    hipLaunchKernelGGL((chunk_final_kernel<false, true>), final_grid(B, H), dim3(256), 0, stream, nullptr, part, N,
+    LAUNCH_OR_RETURN(v_amax_partial_kernel, dim3(nchunk, H, B), dim3(256), 0, stream, v, N, H, nchunk, part);
+    LAUNCH_OR_RETURN((chunk_final_kernel<false, true>), final_grid(B, H), dim3(256), 0, stream, nullptr, part, N,
                        H, nchunk, nullptr, amax, vs);
-    hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)(Npad / kTile), H, B), dim3(256), 0, stream, v, N, H, Npad,
+    LAUNCH_OR_RETURN(quant_v_kernel, dim3((unsigned)(Npad / kTile), H, B), dim3(256), 0, stream, v, N, H, Npad,
                        vs, vc);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 // nr == nullptr: Q and K as given; otherwise their RMSNorm + RoPE transform.
@@ -700,26 +700,26 @@ hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, cons
     // (blocks past N write zero codes and scales); the partials exist for the
     // nchunk blocks that hold tokens
     if (nr)
-        hipLaunchKernelGGL(qkv_pass1_kernel<true>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
+        LAUNCH_OR_RETURN(qkv_pass1_kernel<true>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
                            wsk, wsv);
     else
-        hipLaunchKernelGGL(qkv_pass1_kernel<false>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
+        LAUNCH_OR_RETURN(qkv_pass1_kernel<false>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
                            wsk, wsv);
-    hipLaunchKernelGGL((chunk_final_kernel<true, true>), final_grid(B, H), dim3(256), 0, stream, wsk, wsv, N, H,
+    LAUNCH_OR_RETURN((chunk_final_kernel<true, true>), final_grid(B, H), dim3(256), 0, stream, wsk, wsv, N, H,
                        nchunk, km, amax, vs);
     if (nr)
-        hipLaunchKernelGGL(qkv_pass3_kernel<true>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
+        LAUNCH_OR_RETURN(qkv_pass3_kernel<true>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
                            vc);
     else
-        hipLaunchKernelGGL(qkv_pass3_kernel<false>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
+        LAUNCH_OR_RETURN(qkv_pass3_kernel<false>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
                            vc);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 hipError_t launch_norm_rope(OutView q, OutView k, int B, int N, int H, NormRope nr, hipStream_t stream) {
-    hipLaunchKernelGGL(norm_rope_kernel, dim3((unsigned)((N + 63) / 64 * H * B)), dim3(256), 0, stream, q, k, N, H,
+    LAUNCH_OR_RETURN(norm_rope_kernel, dim3((unsigned)((N + 63) / 64 * H * B)), dim3(256), 0, stream, q, k, N, H,
                        nr);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace sage
