@@ -189,10 +189,10 @@ int sage_quantize_qkv_noalloc(const sage_bf16_in *q, const sage_bf16_in *k, cons
  *   y_d = (x_d * r) * gamma[d]                       (gamma_q for Q, gamma_k for K)
  *   (y_2i, y_2i+1) <- (y_2i c - y_2i+1 s,  y_2i s + y_2i+1 c),  (c, s) = rope[n][i]
  *   x <- bf16(y), round to nearest even.
- * fp32 arithmetic, every product and sum rounded (no fused multiply-add), IEEE
- * sqrt and division; ss adds the squares of 8 consecutive channels left to right
- * and combines the 16 partials as a pairwise tree in channel order
- * ((p0 + p1) + (p2 + p3)) + ...  The result is bit-exactly defined by this.
+ * ss is the exact sum of the squares of the bf16 inputs rounded once to fp32
+ * (nearest even; +inf beyond the fp32 range), so no summation order enters; the
+ * rest is fp32 arithmetic, every product and sum rounded (no fused multiply-add),
+ * IEEE sqrt and division.  The result is bit-exactly defined by this.
  *   q, k: [B, N, H, D] views written in place: 16-byte aligned, strides
  *     multiples of 8, distinct (b, n, h) rows (else SAGE_ERR_STRIDE); Q and K
  *     must not share elements (not checked).

@@ -82,7 +82,9 @@ def _load():
         lib.sage_oracle_mx_quantize.argtypes = [_p, _i64, _int, _int, _p, _p]
         lib.sage_oracle_mx_quantize.restype = None
         lib.sage_oracle_norm_rope.argtypes = [_p, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p,
-                                              ctypes.c_float, _int, _p]
+                                              ctypes.c_float, _p]
+        lib.sage_oracle_sum_squares.argtypes = [_p, _i64, _int, _p]
+        lib.sage_oracle_sum_squares.restype = None
         lib.sage_oracle_norm_rope.restype = None
         lib.sage_oracle_norm_rope_f64.argtypes = [_p, _i64, _i64, _i64, _int, _int, _int, _int, _p, _p, _dbl, _p]
         lib.sage_oracle_norm_rope_f64.restype = None
@@ -304,16 +306,27 @@ def mx_dequantize(codes, scales, fmt: int) -> np.ndarray:
     return el * np.repeat(sc, 32, axis=-1)
 
 
-def norm_rope(x: View, gamma, rope, eps: float, chunk: int = 8) -> np.ndarray:
+def norm_rope(x: View, gamma, rope, eps: float) -> np.ndarray:
     """RMSNorm over each head row's D channels (weight gamma[D]) then RoPE on
-    channel pairs (2i, 2i+1) with rope[n, i] = (cos, sin), in the fixed fp32
-    order written out in sage_oracle.c; bf16 result bits, [B, N, H, D] uint16."""
+    channel pairs (2i, 2i+1) with rope[n, i] = (cos, sin): the sum of squares
+    exact and rounded once to fp32, the rest in the fp32 steps written out in
+    sage_oracle.c; bf16 result bits, [B, N, H, D] uint16."""
     g, pg = _c(np.asarray(gamma, np.float32).reshape(-1), np.float32)
     r, pr = _c(np.asarray(rope, np.float32), np.float32)
     assert g.size == x.D and r.shape == (x.N, x.D // 2, 2)
     out = np.empty((x.B, x.N, x.H, x.D), np.uint16)
-    _load().sage_oracle_norm_rope(*x.args(), x.B, x.N, x.H, x.D, pg, pr, float(np.float32(eps)), chunk,
-                                  out.ctypes.data)
+    _load().sage_oracle_norm_rope(*x.args(), x.B, x.N, x.H, x.D, pg, pr, float(np.float32(eps)), out.ctypes.data)
+    return out
+
+
+def sum_squares(bits) -> np.ndarray:
+    """The exact sum of the squares of each row of bf16 values (uint16 bit patterns, [..., n]), rounded once
+    to fp32 (nearest even): the norm's ss."""
+    b, pb = _c(np.asarray(bits, np.uint16), np.uint16)
+    n = b.shape[-1]
+    rows = b.size // n
+    out = np.empty(b.shape[:-1], np.float32)
+    _load().sage_oracle_sum_squares(pb, rows, n, out.ctypes.data)
     return out
 
 

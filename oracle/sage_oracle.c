@@ -559,35 +559,97 @@ void sage_oracle_attn_int8qk(const int8_t *qc, const float *qs, const int8_t *kc
  *     (a, b) -> (a cos - b sin, a sin + b cos);
  *   - the result stored as bf16, rounded once (nearest even).
  *
- * The bf16 result decides INT8 codes downstream, so the fp32 arithmetic is
- * written out with a fixed order (the order the GPU kernel uses):
- *   ss  = the squares of `chunk` consecutive channels summed left to right, the
- *         D/chunk partial sums then combined as a pairwise tree in channel order
- *         ((s0+s1)+(s2+s3))+...;
+ * The bf16 result decides INT8 codes downstream, so the fp32 evaluation is
+ * written out:
+ *   ss  = the exact sum of the squares x_d^2, rounded once to fp32 (nearest,
+ *         ties to even; +inf beyond the largest finite value): no summation
+ *         order enters;
  *   r   = 1 / sqrtf(ss / D + eps)          (IEEE sqrt and division)
  *   n_d = (x_d * r) * gamma_d
  *   y   = (n_2i * c - n_2i+1 * s,  n_2i * s + n_2i+1 * c)
- * every operation rounded to fp32, none fused.  D/chunk must be a power of 2. */
-static float sum_squares_f32(const float *x, int D, int chunk)
+ * every operation after ss rounded to fp32, none fused. */
+
+/* A bf16 value (exactly representable in x) is +-M * 2^(E - 134) with E its
+ * biased exponent field and M <= 255 an integer (the hidden bit included; a
+ * subnormal has E = 0 and is read as E = 1 without the hidden bit), so its
+ * square M^2 * 2^(2E - 268) is a whole number of units of 2^-266.  The squares
+ * of a row are added as integers in a fixed-point accumulator of 9 64-bit words
+ * (the largest possible row sum, 512 squares of the largest finite bf16 value
+ * 255^2 * 2^506 each, stays below 2^531 < 2^576), and the total is rounded to
+ * fp32 once. */
+#define SQ_WORDS 9
+
+static void sq_add(uint64_t *acc, uint32_t m2, int shift)
 {
-    float part[64];
-    int m = D / chunk;
-    for (int c = 0; c < m; c++) {
-        float a = 0.0f;
-        for (int j = 0; j < chunk; j++) {
-            float sq = x[c * chunk + j] * x[c * chunk + j];
-            a = (j == 0) ? sq : a + sq;
-        }
-        part[c] = a;
+    int w = shift / 64, off = shift % 64;
+    uint64_t lo = (uint64_t)m2 << off;
+    uint64_t hi = off > 48 ? (uint64_t)m2 >> (64 - off) : 0;   /* m2 < 2^16 */
+    uint64_t old = acc[w];
+    acc[w] = old + lo;
+    uint64_t carry = acc[w] < old;
+    for (int i = w + 1; i < SQ_WORDS && (hi | carry); i++) {
+        old = acc[i];
+        acc[i] = old + hi + carry;        /* hi + carry <= 2^16: wraps iff the word decreases */
+        carry = acc[i] < old;
+        hi = 0;
     }
-    for (int w = 1; w < m; w *= 2)          /* pairwise: (0,1), (2,3), ... then ((0,1),(2,3)), ... */
-        for (int c = 0; c < m; c += 2 * w)
-            part[c] = part[c] + part[c + w];
-    return part[0];
+}
+
+static int sq_bit(const uint64_t *acc, int i)
+{
+    return (int)((acc[i / 64] >> (i % 64)) & 1u);
+}
+
+static float exact_sum_squares_f32(const float *x, int n)
+{
+    uint64_t acc[SQ_WORDS];
+    memset(acc, 0, sizeof acc);
+    for (int d = 0; d < n; d++) {
+        uint32_t u;
+        memcpy(&u, &x[d], 4);
+        uint32_t e = (u >> 23) & 0xFF, m = (u >> 16) & 0x7F;
+        if (e == 0 && m == 0)
+            continue;
+        if (e == 0)
+            e = 1;                       /* subnormal: no hidden bit */
+        else
+            m |= 0x80;
+        sq_add(acc, m * m, 2 * (int)e - 2);
+    }
+    int t = -1;                          /* the highest set bit */
+    for (int i = 64 * SQ_WORDS - 1; i >= 0 && t < 0; i--)
+        if (sq_bit(acc, i))
+            t = i;
+    if (t < 0)
+        return 0.0f;
+    /* keep 24 significant bits, or the bits at or above the fp32 subnormal
+     * quantum 2^-149 = bit 117 of the accumulator */
+    int p = t - 23 > 117 ? t - 23 : 117;
+    uint32_t q = 0;
+    for (int i = t; i >= p; i--)
+        q = (q << 1) | (uint32_t)sq_bit(acc, i);
+    int half = p > 0 ? sq_bit(acc, p - 1) : 0, sticky = 0;
+    for (int i = p - 2; i >= 0 && !sticky; i--)
+        sticky = sq_bit(acc, i);
+    if (half && (sticky || (q & 1u)))
+        q++;
+    return ldexpf((float)q, p - 266);    /* exact, or +inf past the fp32 range */
+}
+
+/* The exact-sum rounding alone, for its pins: rows x n bf16 bit patterns. */
+void sage_oracle_sum_squares(const uint16_t *bits, i64 rows, int n, float *out)
+{
+    float *x = malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+    for (i64 r = 0; r < rows; r++) {
+        for (int d = 0; d < n; d++)
+            x[d] = bf16_to_f32(bits[r * n + d]);
+        out[r] = exact_sum_squares_f32(x, n);
+    }
+    free(x);
 }
 
 void sage_oracle_norm_rope(const uint16_t *x, i64 sb, i64 sn, i64 sh, int B, int N, int H, int D,
-                           const float *gamma, const float *rope, float eps, int chunk, uint16_t *out)
+                           const float *gamma, const float *rope, float eps, uint16_t *out)
 {
 #pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; b++)
@@ -595,7 +657,7 @@ void sage_oracle_norm_rope(const uint16_t *x, i64 sb, i64 sn, i64 sh, int B, int
             for (int h = 0; h < H; h++) {
                 float xr[512], nr[512];
                 for (int d = 0; d < D; d++) xr[d] = load_bf16(x, sb, sn, sh, b, n, h, d);
-                float ss = sum_squares_f32(xr, D, chunk);
+                float ss = exact_sum_squares_f32(xr, D);
                 float r = 1.0f / sqrtf(ss / (float)D + eps);
                 for (int d = 0; d < D; d++) nr[d] = (xr[d] * r) * gamma[d];
                 uint16_t *o = out + (((i64)b * N + n) * H + h) * D;

@@ -126,15 +126,13 @@ __device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (
 // "gb10-sage-strided-nhd-summary-1344x768-124f-seed440420.json",
 // dataflow.qk_transform: Q and K pass through RMSNorm and rotary embedding on
 // their strided views before quantisation.  Per (b, n, h) row of D = 128:
-//   r = 1 / sqrt(sum_d x_d^2 / D + eps),  y_d = (x_d * r) * gamma_d,
+//   ss = sum_d x_d^2, exact, rounded once to fp32 (nearest even),
+//   r = 1 / sqrt(ss / D + eps),  y_d = (x_d * r) * gamma_d,
 //   channel pairs (2i, 2i+1) turned by the token's angle: (a c - b s, a s + b c),
 // rounded once to bf16.  The 16 threads of a row are 16 consecutive lanes
-// (seg = lane % 16, channels 8*seg..+7).  Each adds the squares of its 8
-// channels left to right; an xor butterfly over the 16 lanes then combines the
-// partials as a pairwise tree in channel order (every lane ends with the same
-// bits: fp32 addition is commutative).  No contraction (see the pragma above):
-// every product and sum is rounded to fp32, so the result is bit-exactly
-// defined.
+// (seg = lane % 16, channels 8*seg..+7).  No contraction (see the pragma above)
+// after ss: every product and sum is rounded to fp32, so the result is
+// bit-exactly defined.
 
 // Lane-permuted copy of a within each 16-lane row (DPP; all lanes active).
 template <int CTRL>
@@ -142,17 +140,126 @@ __device__ __forceinline__ float dpp_f32(float a) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false));
 }
 
-// The xor butterfly over the 16 lanes of a row, partner offsets 1, 2, 4, 8, with
-// DPP: quad permutations reach the offset-1 and offset-2 partners; once each quad
-// holds one value, the half-row mirror reaches a lane of the offset-4 partner
-// quad, and once each half-row holds one value, the row mirror reaches the other
-// half.  Every step adds the same two values as the xor partner would.
-__device__ __forceinline__ float row16_sum(float a) {
-    a = a + dpp_f32<0xB1>(a);    // quad_perm [1, 0, 3, 2]: lane ^ 1
-    a = a + dpp_f32<0x4E>(a);    // quad_perm [2, 3, 0, 1]: lane ^ 2
-    a = a + dpp_f32<0x141>(a);   // row_half_mirror: the other quad of the half-row
-    a = a + dpp_f32<0x140>(a);   // row_mirror: the other half of the row
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t a) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double a) {
+    const uint64_t u = __double_as_longlong(a);
+    const uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Reductions over the 16 lanes of a row with DPP: quad permutations reach the
+// xor-1 and xor-2 partners; once each quad holds one value, the half-row mirror
+// reaches a lane of the other quad of the half-row, and once each half-row holds
+// one value, the row mirror reaches the other half.  Every lane ends with the
+// row's result.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t a) {
+    a = max(a, dpp_u32<0xB1>(a));    // quad_perm [1, 0, 3, 2]
+    a = max(a, dpp_u32<0x4E>(a));    // quad_perm [2, 3, 0, 1]
+    a = max(a, dpp_u32<0x141>(a));   // row_half_mirror
+    a = max(a, dpp_u32<0x140>(a));   // row_mirror
     return a;
+}
+__device__ __forceinline__ uint32_t row16_min_u32(uint32_t a) {
+    a = min(a, dpp_u32<0xB1>(a));
+    a = min(a, dpp_u32<0x4E>(a));
+    a = min(a, dpp_u32<0x141>(a));
+    a = min(a, dpp_u32<0x140>(a));
+    return a;
+}
+__device__ __forceinline__ double row16_sum_f64(double a) {
+    a = a + dpp_f64<0xB1>(a);
+    a = a + dpp_f64<0x4E>(a);
+    a = a + dpp_f64<0x141>(a);
+    a = a + dpp_f64<0x140>(a);
+    return a;
+}
+
+// ---- ss: the exact sum of a row's squares, rounded once to fp32
+// A bf16 value is +-M * 2^(E - 134) with E its exponent field and M <= 255 (the
+// hidden bit included; a subnormal reads as E = 1 without it), so its square is
+// M^2 * 2^(2E - 268).
+//  * Fast path: if the row's nonzero values span at most 15 exponents
+//    (E_max - E_min <= 15), every square is a multiple of 2^(2 E_min - 268) and
+//    every partial sum of the 128 squares is below 2^(2 E_max - 245), which needs
+//    at most 2 (E_max - E_min) + 23 <= 53 bits: the fp64 sum is exact in any
+//    order and one conversion rounds it.
+//  * Other rows (a nonzero value 2^15 or more below the row's largest: about one
+//    Gaussian row in a hundred) add the squares as integers in LDS, 18 32-bit
+//    words in units of 2^-266 (512 squares of the largest bf16 stay below
+//    2^531), by atomic adds whose carries ripple upward, and round the total.
+constexpr int kSqWords = 18;
+
+// The exact total of the words at w (this row group's 18 LDS words), rounded
+// to fp32: 24 significant bits or the bits at or above 2^-149 (word bit 117),
+// nearest even; the fp32 bit pattern (q carries into the exponent by itself).
+__device__ uint32_t sq_words_to_f32(const uint32_t *w) {
+    int t = -1;
+    for (int i = kSqWords - 1; i >= 0 && t < 0; i--) {
+        const uint32_t v = w[i];
+        if (v) t = 32 * i + 31 - __builtin_clz(v);
+    }
+    if (t < 0) return 0u;
+    const int p = max(t - 23, 117), pm = p - 1;            // pm: the rounding bit
+    const int w0 = pm >> 5, sh = pm & 31;
+    const uint64_t win = (((uint64_t)w[w0 + 1] << 32) | w[w0]) >> sh;   // bits pm .. pm + 32 + (31 - sh)
+    bool sticky = (w[w0] & ((1u << sh) - 1u)) != 0u;
+    for (int i = 0; i < w0; i++) sticky = sticky || w[i] != 0u;
+    uint32_t q = (uint32_t)(win >> 1) & 0x1FFFFFFu;         // bits p .. t (t - p <= 23)
+    if ((win & 1u) && (sticky || (q & 1u))) q++;
+    const uint32_t bits = ((uint32_t)(p - 117) << 23) + q;
+    return bits >= 0x7F800000u ? 0x7F800000u : bits;
+}
+
+// The slow path for one row group (all 16 of its lanes active, 8 values each).
+__device__ float ss_exact_lds(const float (&x)[8], uint32_t *w, int seg) {
+    w[seg] = 0u;
+    if (seg < kSqWords - 16) w[16 + seg] = 0u;
+    __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): the zeros are in LDS
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t u = __float_as_uint(x[j]);
+        uint32_t e = (u >> 23) & 0xFFu, m = (u >> 16) & 0x7Fu;
+        if (e == 0u && m == 0u) continue;
+        if (e == 0u) e = 1u;
+        else m |= 0x80u;
+        const uint32_t sq = m * m;                         // < 2^16
+        const int s = 2 * (int)e - 2, wi = s >> 5, off = s & 31;
+        const uint32_t lo = sq << off, hi = off > 16 ? sq >> (32 - off) : 0u;
+        uint32_t old = atomicAdd(&w[wi], lo);
+        uint32_t v = hi + (uint32_t)(old + lo < old);      // the carry out of the low word
+        for (int k = wi + 1; v != 0u && k < kSqWords; k++) {
+            old = atomicAdd(&w[k], v);
+            v = (uint32_t)(old + v < old);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    return __uint_as_float(sq_words_to_f32(w));
+}
+
+// ss of one row whose 8 values this lane holds (all 16 lanes of the row call it).
+__device__ __forceinline__ float row_sum_squares(const float (&x)[8], uint32_t *words, int seg) {
+    uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+    double s = 0.0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        const uint32_t mag = (__float_as_uint(x[j]) >> 16) & 0x7FFFu;   // bf16 magnitude bits (ordered)
+        hi = max(hi, mag);
+        lo = min(lo, mag - 1u);                             // 0 -> 0xFFFFFFFF: zeros never set the minimum
+        const double d = (double)x[j];
+        s = __builtin_fma(d, d, s);                         // the squares are exact in fp64
+    }
+    hi = row16_max_u32(hi);
+    lo = row16_min_u32(lo);
+    s = row16_sum_f64(s);
+    const int emax = max((int)(hi >> 7), 1), emin = max((int)((lo + 1u) >> 7), 1);
+    if (hi == 0u || emax - emin <= 15) return (float)s;    // exact fp64 sum, rounded once
+    return ss_exact_lds(x, words, seg);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -194,15 +301,12 @@ template <int R>
 __device__ __forceinline__ void norm_rope_rows(float (&x)[R][8], const float *const (&gamma)[R], const int (&n)[R],
                                                const NormRope &nr, int N, uint4 (&out)[R]) {
     static_assert(R == 4 || R == 8, "rows per lane");
+    __shared__ uint32_t sq_words[16][kSqWords];            // per 16-lane row group (256 threads)
     const int seg = threadIdx.x & 15;
+    uint32_t *words = sq_words[(threadIdx.x >> 4) & 15];
     float ss[R];
 #pragma unroll
-    for (int i = 0; i < R; i++) {
-        float a = x[i][0] * x[i][0];
-#pragma unroll
-        for (int j = 1; j < 8; j++) a = a + x[i][j] * x[i][j];
-        ss[i] = row16_sum(a);
-    }
+    for (int i = 0; i < R; i++) ss[i] = row_sum_squares(x[i], words, seg);
     float a = ss[0];
 #pragma unroll
     for (int i = 1; i < R; i++) a = (seg % R == i) ? ss[i] : a;

@@ -1,8 +1,10 @@
 """RMSNorm + RoPE of Q and K on the GPU through the C ABI.
 
 * sage_qk_norm_rope (in place): the transformed Q and K equal the oracle's
-  fixed-order fp32 evaluation bit for bit, on HND and packed strided views,
-  ragged N and the block-24 workload; nothing outside the two views changes.
+  evaluation (the exact sum of squares rounded once to fp32, then fixed fp32
+  steps) bit for bit, on HND and packed strided views, ragged N, the block-24
+  workload and rows built to take the kernel's exact integer path; nothing
+  outside the two views changes.
 * sage_quantize_qkv_rope (fused): every code, scale and k_mean equals the
   oracle's quantisers applied to the oracle's transformed Q and K, bit for bit,
   and equals sage_qk_norm_rope followed by sage_quantize_qkv on the GPU; the
@@ -148,3 +150,47 @@ def test_norm_rope_extreme_rows_bitexact():
         sage.quantize_qkv_rope(g2.q, g2.k, g2.v, nr.to("cuda"), buf)
         torch.cuda.synchronize()
         G.check_quant_bitexact(buf, ref)
+
+
+def test_norm_rope_exact_sum_rows_bitexact():
+    """Rows whose sum of squares an fp64 sum cannot round correctly (ties broken by a square far below the
+    fp64 ulp), rows spanning the whole bf16 exponent range (the exact integer path of the kernel), rows
+    whose squares overflow fp32, in blocks where every 16-lane row group takes the exact path at once and
+    in blocks where only some do: in place and fused, bit-exact against the oracle."""
+    B, N, H, D = 1, 192, 3, 128
+    rng = np.random.default_rng(29)
+    x = rng.standard_normal((B, N, 3 * H, D))
+    tie = np.zeros(D)
+    tie[:2] = (1.0, 2.0 ** -12)                                       # 1 + 2^-24: a tie, rounds to even
+    broken = tie.copy()
+    broken[2] = 2.0 ** -60                                            # + 2^-120: rounds up
+    odd = np.zeros(D)
+    odd[:4] = (1.0, 2.0 ** -12, 2.0 ** -12, 2.0 ** -12)              # a tie above an odd value
+    for n in range(0, 64):                                            # block 0: every row takes the exact path
+        x[0, n] = rng.standard_normal((3 * H, D)) * np.exp2(rng.integers(-133, 100, (3 * H, D)).astype(np.float64))
+    for n in range(64, 128):                                          # block 1: constructed rows, mixed
+        kind = n % 4
+        if kind == 0:
+            x[0, n, :, :] = broken * rng.choice([1.0, 2.0 ** 20, 2.0 ** -40], (3 * H, 1))
+        elif kind == 1:
+            x[0, n, :, :] = tie
+        elif kind == 2:
+            x[0, n, :, :] = odd * 2.0 ** -30
+    x[0, 130] = 2.0 ** 70                                             # squares past the fp32 range
+    x[0, 131, :, :8] = 2.0 ** -133                                    # subnormals beside normal values
+    packed = torch.from_numpy(x.reshape(B, N, 3 * H * D)).float().to(torch.bfloat16)
+    HD = H * D
+    q, k, v = (packed[:, :, i * HD:(i + 1) * HD].unflatten(2, (H, D)) for i in range(3))
+    case = inputs.Case("exact_sum", B, N, H, D, q, k, v, packed)
+    nr = inputs.norm_rope_params(N, seed=10)
+    want = _oracle_transformed(case, nr)
+    g = G.gpu_case(case)
+    sage.sage_qk_norm_rope(g.q, g.k, nr.to("cuda").gamma_q, nr.to("cuda").gamma_k, nr.rope.cuda(), nr.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(g.q.cpu().view(torch.int16), want.q.view(torch.int16)), "Q"
+    assert torch.equal(g.k.cpu().view(torch.int16), want.k.view(torch.int16)), "K"
+    g2 = G.gpu_case(case)
+    buf = sage.Buffers(B, N, H)
+    sage.quantize_qkv_rope(g2.q, g2.k, g2.v, nr.to("cuda"), buf)
+    torch.cuda.synchronize()
+    G.check_quant_bitexact(buf, G.OracleRef(want))

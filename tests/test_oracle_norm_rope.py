@@ -153,3 +153,90 @@ def test_fp32_order_close_to_fp64(stress):
         # rounding except where fp32 error crosses a rounding boundary
         assert np.all(np.abs(y32 - y64) <= 2.0 ** -8 * np.abs(y64) + 1e-30)
         assert (y32 != bf16(y64)).mean() < 2e-3
+
+
+# ---- the sum of squares: the exact sum, rounded once to fp32 ----------------
+from fractions import Fraction  # noqa: E402
+
+
+def rn32(F: Fraction) -> float:
+    """The fp32 value nearest to the exact non-negative rational F (ties to even; +inf from 2^128 on)."""
+    if F == 0:
+        return 0.0
+    e = F.numerator.bit_length() - F.denominator.bit_length()      # 2^e <= F < 2^(e+2)
+    if Fraction(2) ** e > F:
+        e -= 1
+    p = max(e - 23, -149)                                              # the fp32 quantum at F
+    scaled = F / Fraction(2) ** p
+    q = scaled.numerator // scaled.denominator
+    rem = scaled - q
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and q % 2 == 1):
+        q += 1
+    v = Fraction(q) * Fraction(2) ** p
+    return float("inf") if v >= Fraction(2) ** 128 else float(v)      # exact: an fp32 value fits in fp64
+
+
+def exact_ss(bits) -> Fraction:
+    vals = (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return sum((Fraction(float(v)) ** 2 for v in vals), Fraction(0))
+
+
+def bits_of(x):
+    return (bf16(x).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _rows_to_check():
+    rng = np.random.default_rng(21)
+    rows = [bits_of(rng.standard_normal(D) * 2.0 ** rng.integers(-60, 60)) for _ in range(120)]
+    # exponents spread over the whole bf16 range, subnormals included
+    for _ in range(40):
+        rows.append(bits_of(rng.standard_normal(D) * np.exp2(rng.integers(-140, 120, D).astype(np.float64))))
+    # squares past the fp32 range (ss = +inf) and just inside it
+    rows.append(bits_of(np.full(D, 2.0 ** 70)))
+    rows.append(bits_of(np.r_[2.0 ** 63 * 1.5, np.zeros(D - 1)]))
+    # exact ties between two fp32 values, and ties broken by a square 2^96 times smaller than the ulp
+    one_tie = np.zeros(D)
+    one_tie[:2] = (1.0, 2.0 ** -12)                       # 1 + 2^-24: halfway between 1 and 1 + 2^-23
+    rows.append(bits_of(one_tie))
+    broken = one_tie.copy()
+    broken[2] = 2.0 ** -60                                 # 1 + 2^-24 + 2^-120: rounds up
+    rows.append(bits_of(broken))
+    odd_tie = np.zeros(D)
+    odd_tie[:4] = (1.0, 2.0 ** -12, 2.0 ** -12, 2.0 ** -12)    # 1 + 3 * 2^-24: halfway above an odd value
+    rows.append(bits_of(odd_tie))
+    rows.append(np.zeros(D, np.uint16))                    # all zero (and -0)
+    rows.append(np.full(D, 0x8000, np.uint16))
+    rows.append(np.arange(1, D + 1, dtype=np.uint16))      # bf16 subnormals only: ss is an fp32 subnormal or 0
+    return np.stack(rows)
+
+
+def test_sum_squares_is_the_rounded_exact_sum():
+    rows = _rows_to_check()
+    got = oracle.sum_squares(rows)
+    want = np.array([rn32(exact_ss(r)) for r in rows], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    assert np.isinf(got[120 + 40]) and np.isfinite(got[120 + 41])
+    tie, broken, odd = got[162], got[163], got[164]
+    assert tie == 1.0 and broken == np.float32(1 + 2.0 ** -23) and odd == np.float32(1 + 2.0 ** -22)
+
+
+def test_sum_squares_is_not_an_fp64_sum():
+    # the tie-breaking square is far below an fp64 ulp of the total: an fp64 sum in any order, rounded
+    # to fp32, lands on the tie and rounds to even, while the exact sum rounds up
+    row = _rows_to_check()[163]
+    sq = ((row.astype(np.uint32) << 16).view(np.float32).astype(np.float64)) ** 2
+    assert np.float32(sq.sum()) == 1.0 and np.float32(sq[::-1].sum()) == 1.0
+    assert oracle.sum_squares(row[None])[0] == np.float32(1 + 2.0 ** -23)
+
+
+def test_norm_uses_the_exact_sum():
+    # the transform of the tie-broken row equals the formula evaluated with rn32(exact sum) for ss
+    row = _rows_to_check()[163].astype(np.uint32)
+    x = (row << 16).view(np.float32)
+    view = oracle.View.from_bnhd(row.astype(np.uint16).reshape(1, 1, 1, D))
+    eps = np.float32(1e-6)
+    got = oracle.norm_rope(view, np.ones(D), identity_table(1), float(eps))
+    ss = np.float32(rn32(exact_ss(row.astype(np.uint16))))
+    r = np.float32(1.0) / np.sqrt(np.float32(ss / np.float32(D) + eps))
+    want = bits_of((x * r) * np.float32(1.0))
+    assert np.array_equal(got.reshape(-1), want)
