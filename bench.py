@@ -497,6 +497,10 @@ def main():
     er = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.bf16_calls)]
     sage.quantize_qkv_rope(g.q, g.k, g.v, nr, rbuf, stream)
     for e in er:
+        # each in-place transform starts from the workload's own Q and K (transforming the same buffer again
+        # and again would multiply channel d by gamma_d per call and drift far from the workload)
+        with torch.cuda.stream(stream):
+            pk.copy_(g.packed)
         e[0].record(stream)
         sage.sage_qk_norm_rope(pq, pk_k, nr.gamma_q, nr.gamma_k, nr.rope, nr.eps, stream)
         e[1].record(stream)

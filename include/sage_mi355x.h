@@ -71,7 +71,8 @@ extern "C" {
 typedef enum {
     SAGE_OK = 0,
     SAGE_ERR_NULL = 1,      /* a required pointer is NULL */
-    SAGE_ERR_SHAPE = 2,     /* B, N, H < 1, D != 128, or sizes overflow */
+    SAGE_ERR_SHAPE = 2,     /* B, N, H < 1, D != 128, B or H > 65535, or
+                               B * H * Npad > 2^29 - 1 (launch sizes) */
     SAGE_ERR_STRIDE = 3,    /* strides let tokens or heads overlap */
     SAGE_ERR_ALIGN = 4,     /* a pointer or stride breaks 16-byte alignment */
     SAGE_ERR_WORKSPACE = 5, /* workspace too small */
@@ -202,10 +203,17 @@ int sage_quantize_qkv_noalloc(const sage_bf16_in *q, const sage_bf16_in *k, cons
 int sage_qk_norm_rope(const sage_bf16_out *q, const sage_bf16_out *k, int B, int N, int H, int D,
                       const float *gamma_q, const float *gamma_k, const float *rope, float eps, void *stream);
 
+/* Bytes of device workspace sage_quantize_qkv_rope needs:
+ * sage_qkv_workspace_bytes(B, N, H, D) plus B*H*Npad floats (the norm factor r of
+ * every K row, computed by the first pass and reused by the last). */
+size_t sage_qkv_rope_workspace_bytes(int B, int N, int H, int D);
+
 /* sage_qk_norm_rope fused into sage_quantize_qkv: the codes, scales and k_mean
  * that sage_qk_norm_rope followed by sage_quantize_qkv produce, bit for bit, with
  * Q and K read once less and not written (the transformed Q and K are not
- * materialised; q and k are only read).  Arguments as the two calls. */
+ * materialised; q and k are only read).  Arguments as the two calls, except the
+ * workspace: >= sage_qkv_rope_workspace_bytes(B, N, H, D) bytes, 8-byte aligned
+ * (else SAGE_ERR_WORKSPACE / SAGE_ERR_ALIGN). */
 int sage_quantize_qkv_rope(const sage_bf16_in *q, const sage_bf16_in *k, const sage_bf16_in *v, int B, int N, int H,
                            int D, const float *gamma_q, const float *gamma_k, const float *rope, float eps,
                            int8_t *q_codes, float *q_scale, int8_t *k_codes, float *k_scale, float *k_mean,

@@ -43,12 +43,12 @@ int check_shape(int B, int N, int H, int D) {
     if (D != kD) return SAGE_ERR_SHAPE;
     if (B > 65535 || H > 65535) return SAGE_ERR_SHAPE;
     const int64_t npad = ((int64_t)N + SAGE_N_ALIGN - 1) / SAGE_N_ALIGN * SAGE_N_ALIGN;
-    const double bytes = (double)B * H * (double)npad * kD;
-    if (bytes > 4.0e18) return SAGE_ERR_SHAPE;
-    const double blocks = (double)B * H * std::ceil((double)N / 128.0);
-    if (blocks > 4.0e9) return SAGE_ERR_SHAPE;
-    // the quantisers' 1-D grids: one workgroup per (64-token block, head, batch)
-    if ((double)B * H * (double)(npad / 64) > 4.0e9) return SAGE_ERR_SHAPE;
+    // Every launch's work-item count (workgroups x threads) must fit the
+    // dispatch's 32-bit grid size.  The largest is the fused RoPE quantiser's
+    // first pass, 2 B H Npad/64 workgroups of 256 threads = 8 B H Npad work-items
+    // (the other quantiser grids are half that, attention B H ceil(N/128) x 256,
+    // the MX quantiser B N H D/32); this also bounds every tensor's size.
+    if ((double)B * H * (double)npad * 8.0 > 4294967295.0) return SAGE_ERR_SHAPE;
     return SAGE_OK;
 }
 
@@ -148,6 +148,13 @@ size_t sage_qkv_workspace_bytes(int B, int N, int H, int D) {
     const size_t nchunk = (size_t)((N + SAGE_K_BLOCK - 1) / SAGE_K_BLOCK);
     const size_t total = (size_t)B * H * D;
     return nchunk * total * (sizeof(double) + sizeof(float)) + total * sizeof(float);
+}
+
+size_t sage_qkv_rope_workspace_bytes(int B, int N, int H, int D) {
+    const size_t base = sage_qkv_workspace_bytes(B, N, H, D);
+    if (base == 0) return 0;
+    const size_t npad = ((size_t)N + SAGE_N_ALIGN - 1) / SAGE_N_ALIGN * SAGE_N_ALIGN;
+    return base + (size_t)B * H * npad * sizeof(float);
 }
 
 int sage_quantize_qk(const sage_bf16_in *q, const sage_bf16_in *k, int B, int N, int H, int D, int8_t *q_codes,
@@ -278,7 +285,7 @@ int sage_quantize_qkv_rope(const sage_bf16_in *q, const sage_bf16_in *k, const s
     if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) || !aligned(q_scale, 4) ||
         !aligned(k_scale, 4) || !aligned(k_mean, 4) || !aligned(v_scale, 4) || !aligned(workspace, 8))
         return SAGE_ERR_ALIGN;
-    if (workspace_bytes < sage_qkv_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
+    if (workspace_bytes < sage_qkv_rope_workspace_bytes(B, N, H, D)) return SAGE_ERR_WORKSPACE;
     const sage::NormRope nr{gamma_q, gamma_k, rope, eps};
     return hip_status(sage::launch_quantize_qkv(to_view(q), to_view(k), to_view(v), B, N, H, &nr, q_codes, q_scale,
                                                 k_codes, k_scale, k_mean, v_codes, v_scale, workspace,

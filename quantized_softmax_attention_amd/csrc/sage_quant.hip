@@ -113,13 +113,38 @@ __global__ __launch_bounds__(256) void chunk_final_kernel(const double *__restri
     }
 }
 
-// 8 consecutive channels of one token row (a 16-byte load), widened exactly.
-__device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (&x)[8]) {
+// 8 consecutive channels of one token row as raw bf16 (a 16-byte load); zeros
+// when !valid.
+__device__ __forceinline__ uint4 load_raw8(const uint16_t *p, bool valid) {
     uint4 raw = make_uint4(0, 0, 0, 0);
     if (valid) raw = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    return raw;
+}
+
+// 8 packed bf16 values (channel order) widened exactly to fp32.
+__device__ __forceinline__ void widen8(uint4 v, float (&x)[8]) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int j = 0; j < 8; j++) x[j] = bf16_to_f32((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+    for (int j = 0; j < 4; j++) {
+        x[2 * j] = __uint_as_float(w[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+}
+
+__device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (&x)[8]) {
+    widen8(load_raw8(p, valid), x);
+}
+
+// The raw rows of tokens tb * 64 + row + 16 i (i = 0..3) of head h of a view,
+// thread (row, seg) = (t / 16, t % 16) holding channels 8 seg..+7.
+__device__ __forceinline__ void load_block_raw(View a, int b, int h, int tb, int N, uint4 (&raw)[4]) {
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const uint16_t *base = a.data + (int64_t)b * a.sb + (int64_t)h * a.sh + seg * 8;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tb * 64 + row + 16 * i;
+        raw[i] = load_raw8(base + (int64_t)n * a.sn, n < N);
+    }
 }
 
 // ------------------------------------------------ RMSNorm + RoPE of Q and K
@@ -156,18 +181,11 @@ __device__ __forceinline__ double dpp_f64(double a) {
 // reaches a lane of the other quad of the half-row, and once each half-row holds
 // one value, the row mirror reaches the other half.  Every lane ends with the
 // row's result.
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t a) {
-    a = max(a, dpp_u32<0xB1>(a));    // quad_perm [1, 0, 3, 2]
-    a = max(a, dpp_u32<0x4E>(a));    // quad_perm [2, 3, 0, 1]
-    a = max(a, dpp_u32<0x141>(a));   // row_half_mirror
-    a = max(a, dpp_u32<0x140>(a));   // row_mirror
-    return a;
-}
 __device__ __forceinline__ uint32_t row16_min_u32(uint32_t a) {
-    a = min(a, dpp_u32<0xB1>(a));
-    a = min(a, dpp_u32<0x4E>(a));
-    a = min(a, dpp_u32<0x141>(a));
-    a = min(a, dpp_u32<0x140>(a));
+    a = min(a, dpp_u32<0xB1>(a));    // quad_perm [1, 0, 3, 2]
+    a = min(a, dpp_u32<0x4E>(a));    // quad_perm [2, 3, 0, 1]
+    a = min(a, dpp_u32<0x141>(a));   // row_half_mirror
+    a = min(a, dpp_u32<0x140>(a));   // row_mirror
     return a;
 }
 __device__ __forceinline__ double row16_sum_f64(double a) {
@@ -182,13 +200,14 @@ __device__ __forceinline__ double row16_sum_f64(double a) {
 // A bf16 value is +-M * 2^(E - 134) with E its exponent field and M <= 255 (the
 // hidden bit included; a subnormal reads as E = 1 without it), so its square is
 // M^2 * 2^(2E - 268).
-//  * Fast path: if the row's nonzero values span at most 15 exponents
-//    (E_max - E_min <= 15), every square is a multiple of 2^(2 E_min - 268) and
-//    every partial sum of the 128 squares is below 2^(2 E_max - 245), which needs
-//    at most 2 (E_max - E_min) + 23 <= 53 bits: the fp64 sum is exact in any
-//    order and one conversion rounds it.
-//  * Other rows (a nonzero value 2^15 or more below the row's largest: about one
-//    Gaussian row in a hundred) add the squares as integers in LDS, 18 32-bit
+//  * Fast path: every square is a multiple of 2^(2 E_min - 268), E_min the
+//    smallest exponent among the row's nonzero values, and every partial sum of
+//    the squares (all positive) is at most their total, below 2^(e + 1) where e is
+//    the binary exponent of the computed fp64 sum (rounding can only raise it).
+//    If e + 1 - (2 E_min - 268) <= 53, every partial sum fits 53 bits: the fp64
+//    sum was exact, in any order, and one conversion rounds it.
+//  * Other rows (a nonzero value about 2^15 or more below the row's largest: about
+//    one Gaussian row in a hundred) add the squares as integers in LDS, 18 32-bit
 //    words in units of 2^-266 (512 squares of the largest bf16 stay below
 //    2^531), by atomic adds whose carries ripple upward, and round the total.
 constexpr int kSqWords = 18;
@@ -214,15 +233,20 @@ __device__ uint32_t sq_words_to_f32(const uint32_t *w) {
     return bits >= 0x7F800000u ? 0x7F800000u : bits;
 }
 
-// The slow path for one row group (all 16 of its lanes active, 8 values each).
-__device__ float ss_exact_lds(const float (&x)[8], uint32_t *w, int seg) {
+// The slow path for one row group (all 16 of its lanes active, 8 values each);
+// a call, not inlined per row: it is rare, and its code would otherwise repeat
+// in every row of every kernel that normalises.
+struct Row8 {
+    float v[8];
+};
+__device__ __attribute__((noinline)) float ss_exact_lds(Row8 x, uint32_t *w, int seg) {
     w[seg] = 0u;
     if (seg < kSqWords - 16) w[16 + seg] = 0u;
     __builtin_amdgcn_s_waitcnt(0xC07F);                    // lgkmcnt(0): the zeros are in LDS
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const uint32_t u = __float_as_uint(x[j]);
+        const uint32_t u = __float_as_uint(x.v[j]);
         uint32_t e = (u >> 23) & 0xFFu, m = (u >> 16) & 0x7Fu;
         if (e == 0u && m == 0u) continue;
         if (e == 0u) e = 1u;
@@ -243,23 +267,28 @@ __device__ float ss_exact_lds(const float (&x)[8], uint32_t *w, int seg) {
 }
 
 // ss of one row whose 8 values this lane holds (all 16 lanes of the row call it).
-__device__ __forceinline__ float row_sum_squares(const float (&x)[8], uint32_t *words, int seg) {
-    uint32_t hi = 0u, lo = 0xFFFFFFFFu;
+__device__ __forceinline__ float row_sum_squares(uint4 raw, uint32_t *words, int seg) {
+    float x[8];
+    widen8(raw, x);
+    uint32_t lo = 0xFFFFFFFFu;
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
         const uint32_t mag = (__float_as_uint(x[j]) >> 16) & 0x7FFFu;   // bf16 magnitude bits (ordered)
-        hi = max(hi, mag);
         lo = min(lo, mag - 1u);                             // 0 -> 0xFFFFFFFF: zeros never set the minimum
         const double d = (double)x[j];
         s = __builtin_fma(d, d, s);                         // the squares are exact in fp64
     }
-    hi = row16_max_u32(hi);
     lo = row16_min_u32(lo);
     s = row16_sum_f64(s);
-    const int emax = max((int)(hi >> 7), 1), emin = max((int)((lo + 1u) >> 7), 1);
-    if (hi == 0u || emax - emin <= 15) return (float)s;    // exact fp64 sum, rounded once
-    return ss_exact_lds(x, words, seg);
+    if (lo == 0xFFFFFFFFu) return 0.0f;                     // an all-zero row
+    const int emin = max((int)((lo + 1u) >> 7), 1);          // subnormals count as exponent 1
+    const int e = (int)(__double_as_longlong(s) >> 52) - 1023;   // s >= 2^-266 > 0: a normal fp64
+    if (e + 1 - (2 * emin - 268) <= 53) return (float)s;   // exact fp64 sum, rounded once
+    Row8 r;
+#pragma unroll
+    for (int j = 0; j < 8; j++) r.v[j] = x[j];
+    return ss_exact_lds(r, words, seg);
 }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -271,14 +300,6 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&x)[8]) {
     return make_uint4(pk(x[0], x[1]), pk(x[2], x[3]), pk(x[4], x[5]), pk(x[6], x[7]));
 }
 
-__device__ __forceinline__ void unpack_bf16x8(uint4 v, float (&x)[8]) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        x[2 * j] = __uint_as_float(w[j] << 16);
-        x[2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-}
 
 // v from lane I of this lane's 16-lane group (ds_swizzle bit mode within 32
 // lanes: source lane = (lane & 0x10) | I).
@@ -291,49 +312,83 @@ __device__ __forceinline__ void group_bcast_all(float v, float *out, std::intege
     ((out[I] = group_bcast<I>(v)), ...);
 }
 
-// The transform of R rows held by this lane (8 channels each; row i belongs to
-// token n[i] and uses weights gamma[i]), as bf16, zeros for tokens >= N.  Must be
-// called by all 16 lanes of the rows' group.  The factor r = 1/sqrt(ss/D + eps)
-// is evaluated once per row rather than once per lane: lane seg computes it for
-// row seg % R and every lane reads row i's from lane i of its 16-lane group (a
+// This lane's 8 weights (channels 8 seg..+7) of one gamma vector.
+struct Gamma8 {
+    float g[8];
+};
+__device__ __forceinline__ Gamma8 load_gamma8(const float *gamma) {
+    const int seg = threadIdx.x & 15;
+    const float4 g0 = *reinterpret_cast<const float4 *>(gamma + 8 * seg);
+    const float4 g1 = *reinterpret_cast<const float4 *>(gamma + 8 * seg + 4);
+    return Gamma8{{g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w}};
+}
+
+// The rotary (cos, sin) of this lane's channel pairs 4 seg..4 seg+3 for token n;
+// tokens >= N read row N - 1 (their outputs are zeros).
+struct Rope8 {
+    float cs[8];
+};
+__device__ __forceinline__ Rope8 load_rope8(const NormRope &nr, int n, int N) {
+    const int seg = threadIdx.x & 15;
+    const int nc = min(n, N - 1);
+    const float4 *tr = reinterpret_cast<const float4 *>(nr.rope + ((int64_t)nc * (kD / 2) + 4 * seg) * 2);
+    const float4 t0 = tr[0], t1 = tr[1];
+    return Rope8{{t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w}};
+}
+
+// The transform of R rows held by this lane (8 channels each, raw bf16; row i
+// belongs to token n[i], has norm factor r[i] and uses weights ga for i < R / 2,
+// gb for the others), as bf16, zeros for tokens >= N.  Each weight vector is loaded once;
+// rows of one token share their rotary loads.
+template <int R>
+__device__ __forceinline__ void rope_rows(const uint4 (&raw)[R], const float (&r)[R], const float *ga,
+                                          const float *gb, const int (&n)[R], const NormRope &nr, int N,
+                                          uint4 (&out)[R]) {
+    const Gamma8 g[2] = {load_gamma8(ga), load_gamma8(gb)};
+    Rope8 cs[R];
+#pragma unroll
+    for (int i = 0; i < R; i++) cs[i] = load_rope8(nr, n[i], N);
+#pragma unroll
+    for (int i = 0; i < R; i++) {
+        const float *gi = g[i < R / 2 ? 0 : 1].g;
+        float x[8], y[8], z[8];
+        widen8(raw[i], x);
+#pragma unroll
+        for (int j = 0; j < 8; j++) y[j] = (x[j] * r[i]) * gi[j];
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            const float c = cs[i].cs[2 * p], sn = cs[i].cs[2 * p + 1];
+            z[2 * p] = y[2 * p] * c - y[2 * p + 1] * sn;
+            z[2 * p + 1] = y[2 * p] * sn + y[2 * p + 1] * c;
+        }
+        const uint4 v = pack_bf16x8(z);
+        const uint32_t keep = n[i] < N ? 0xFFFFFFFFu : 0u;      // a mask, not a branch
+        out[i] = make_uint4(v.x & keep, v.y & keep, v.z & keep, v.w & keep);
+    }
+}
+
+// rope_rows with the norm factors computed here: r = 1/sqrt(ss/D + eps) of each
+// row (returned in r).  Must be called by all 16 lanes of the rows' group.  r is
+// evaluated once per row rather than once per lane: lane seg computes it for row
+// seg % R and every lane reads row i's from lane i of its 16-lane group (a
 // ds_swizzle broadcast); the value is the same, as every lane holds the same ss.
 template <int R>
-__device__ __forceinline__ void norm_rope_rows(float (&x)[R][8], const float *const (&gamma)[R], const int (&n)[R],
-                                               const NormRope &nr, int N, uint4 (&out)[R]) {
+__device__ __forceinline__ void norm_rope_rows(const uint4 (&raw)[R], const float *ga, const float *gb,
+                                               const int (&n)[R], const NormRope &nr, int N, uint4 (&out)[R],
+                                               float (&r)[R]) {
     static_assert(R == 4 || R == 8, "rows per lane");
     __shared__ uint32_t sq_words[16][kSqWords];            // per 16-lane row group (256 threads)
     const int seg = threadIdx.x & 15;
     uint32_t *words = sq_words[(threadIdx.x >> 4) & 15];
     float ss[R];
 #pragma unroll
-    for (int i = 0; i < R; i++) ss[i] = row_sum_squares(x[i], words, seg);
+    for (int i = 0; i < R; i++) ss[i] = row_sum_squares(raw[i], words, seg);
     float a = ss[0];
 #pragma unroll
     for (int i = 1; i < R; i++) a = (seg % R == i) ? ss[i] : a;
     const float rsel = 1.0f / __builtin_sqrtf(a / (float)kD + nr.eps);
-    float rr[R];
-    group_bcast_all(rsel, rr, std::make_integer_sequence<int, R>{});
-#pragma unroll
-    for (int i = 0; i < R; i++) {
-        const float r = rr[i];
-        const float4 g0 = *reinterpret_cast<const float4 *>(gamma[i] + 8 * seg);
-        const float4 g1 = *reinterpret_cast<const float4 *>(gamma[i] + 8 * seg + 4);
-        const int nc = min(n[i], N - 1);
-        const float4 *tr = reinterpret_cast<const float4 *>(nr.rope + ((int64_t)nc * (kD / 2) + 4 * seg) * 2);
-        const float4 t0 = tr[0], t1 = tr[1];
-        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const float cs[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-        float y[8], z[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) y[j] = (x[i][j] * r) * g[j];
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            const float c = cs[2 * p], s = cs[2 * p + 1];
-            z[2 * p] = y[2 * p] * c - y[2 * p + 1] * s;
-            z[2 * p + 1] = y[2 * p] * s + y[2 * p + 1] * c;
-        }
-        out[i] = n[i] < N ? pack_bf16x8(z) : make_uint4(0, 0, 0, 0);
-    }
+    group_bcast_all(rsel, r, std::make_integer_sequence<int, R>{});
+    rope_rows<R>(raw, r, ga, gb, n, nr, N, out);
 }
 
 // The (64-token block, head, batch) of a workgroup in a 1-D grid of H * nblk * B
@@ -358,19 +413,17 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(OutView q, OutView k, in
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
     uint16_t *qb = q.data + (int64_t)b * q.sb + (int64_t)h * q.sh + seg * 8;
     uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
-    float x[8][8];          // rows 0-3: Q of tokens row + 16 i; rows 4-7: K of the same tokens
+    uint4 x[8];             // rows 0-3: Q of tokens row + 16 i; rows 4-7: K of the same tokens
     int n[8];
-    const float *gamma[8];
 #pragma unroll
     for (int i = 0; i < 4; i++) {
         n[i] = n[4 + i] = tb * 64 + row + 16 * i;
-        gamma[i] = nr.gamma_q;
-        gamma[4 + i] = nr.gamma_k;
-        load_row8(qb + (int64_t)n[i] * q.sn, n[i] < N, x[i]);
-        load_row8(kb + (int64_t)n[i] * k.sn, n[i] < N, x[4 + i]);
+        x[i] = load_raw8(qb + (int64_t)n[i] * q.sn, n[i] < N);
+        x[4 + i] = load_raw8(kb + (int64_t)n[i] * k.sn, n[i] < N);
     }
     uint4 y[8];
-    norm_rope_rows<8>(x, gamma, n, nr, N, y);
+    float r[8];
+    norm_rope_rows<8>(x, nr.gamma_q, nr.gamma_k, n, nr, N, y, r);
 #pragma unroll
     for (int i = 0; i < 4; i++)
         if (n[i] < N) {
@@ -480,28 +533,30 @@ __device__ __forceinline__ void store_int8_codes(const float (&x)[4][8], float s
         store_int8_codes_as<false>(x, s_lo, s_hi, tb, bh, Npad, codes);
 }
 
-// K of the block, smoothed: x = fp32(k) - k_mean (one fp32 subtraction); zero
-// for tokens >= N.  ROPE: k is first replaced by its RMSNorm + RoPE transform.
+// K of the block (raw rows from load_block_raw), smoothed: x = fp32(k) - k_mean
+// (one fp32 subtraction); zero for tokens >= N.  ROPE: k is first replaced by its
+// RMSNorm + RoPE transform, with the rows' norm factors kr[bh * Npad + n] as the
+// first pass computed them.
 template <bool ROPE>
-__device__ __forceinline__ void load_k_smoothed(View k, int b, int h, int tb, int N, const float *__restrict__ km,
-                                                int64_t bh, const NormRope &nr, float (&x)[4][8]) {
+__device__ __forceinline__ void k_smoothed(const uint4 (&raw)[4], int tb, int N, const float *__restrict__ km,
+                                           int64_t bh, const NormRope &nr, const float *__restrict__ kr,
+                                           int64_t Npad, float (&x)[4][8]) {
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
-    const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
     float mean[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) mean[j] = km[bh * kD + seg * 8 + j];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int n = tb * 64 + row + 16 * i;
-        load_row8(kb + (int64_t)n * k.sn, n < N, x[i]);
-    }
     if (ROPE) {
-        const float *gamma[4] = {nr.gamma_k, nr.gamma_k, nr.gamma_k, nr.gamma_k};
         const int n[4] = {tb * 64 + row, tb * 64 + row + 16, tb * 64 + row + 32, tb * 64 + row + 48};
-        uint4 y[4];
-        norm_rope_rows<4>(x, gamma, n, nr, N, y);
+        float r[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) unpack_bf16x8(y[i], x[i]);
+        for (int i = 0; i < 4; i++) r[i] = kr[bh * Npad + n[i]];
+        uint4 y[4];
+        rope_rows<4>(raw, r, nr.gamma_k, nr.gamma_k, n, nr, N, y);
+#pragma unroll
+        for (int i = 0; i < 4; i++) widen8(y[i], x[i]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++) widen8(raw[i], x[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -531,8 +586,10 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(View q, View k, int N, in
     const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * H + h;
     float xq[4][8], xk[4][8];
+    uint4 rk[4];
+    load_block_raw(k, b, h, tb, N, rk);
     load_block(q, b, h, tb, N, xq);
-    load_k_smoothed<false>(k, b, h, tb, N, km, bh, NormRope{}, xk);
+    k_smoothed<false>(rk, tb, N, km, bh, NormRope{}, nullptr, Npad, xk);
     float m[3];
     q_local_max(xq, m[0], m[1]);
     m[2] = k_local_max(xk);
@@ -586,21 +643,28 @@ __global__ __launch_bounds__(256) void v_amax_partial_kernel(View v, int N, int 
 // where p0 inverts kappa (see the public header): keys 4g..4g+3 sit at
 // p0 = 32*(g%2) + 16*(g/8) + 4*((g/2)%4).  The 8 KB tile is assembled in LDS
 // (tile: kD x 16 words) and written out with coalesced 16-byte stores.
-__device__ __forceinline__ void v_tile_codes(View v, int b, int h, int tt, int N, int64_t bh, int64_t Npad,
+// The raw V rows thread (g, seg) encodes: keys 4g..4g+3 of tile tt.
+__device__ __forceinline__ void load_v_tile_raw(View v, int b, int h, int tt, int N, uint4 (&raw)[4]) {
+    const int t = threadIdx.x, g = t >> 4, seg = t & 15;
+    const uint16_t *base = v.data + (int64_t)b * v.sb + (int64_t)h * v.sh + seg * 8;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int n = tt * kTile + 4 * g + i;
+        raw[i] = load_raw8(base + (int64_t)n * v.sn, n < N);
+    }
+}
+
+__device__ __forceinline__ void v_tile_codes(const uint4 (&raw)[4], int tt, int N, int64_t bh, int64_t Npad,
                                              const float *__restrict__ vs, uint8_t *__restrict__ vc,
                                              uint32_t (*tile)[kTile / 4]) {
     const int t = threadIdx.x, g = t >> 4, seg = t & 15;
-    const uint16_t *base = v.data + (int64_t)b * v.sb + (int64_t)h * v.sh + seg * 8;
     float sv[8];
 #pragma unroll
     for (int j = 0; j < 8; j++) sv[j] = vs[bh * kD + seg * 8 + j];
     uint32_t packed[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     float x[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {             // all four rows in flight before any is encoded
-        const int n = tt * kTile + 4 * g + i;
-        load_row8(base + (int64_t)n * v.sn, n < N, x[i]);
-    }
+    for (int i = 0; i < 4; i++) widen8(raw[i], x[i]);
     bool fast = true;                         // every channel scale of this thread large enough
 #pragma unroll
     for (int j = 0; j < 8; j++) fast = fast && sv[j] >= kFastDivMin;
@@ -642,7 +706,9 @@ __global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int6
                                                       uint8_t *__restrict__ vc) {
     __shared__ uint32_t tile[kD][kTile / 4];
     const int tt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    v_tile_codes(v, b, h, tt, N, (int64_t)b * H + h, Npad, vs, vc, tile);
+    uint4 rv[4];
+    load_v_tile_raw(v, b, h, tt, N, rv);
+    v_tile_codes(rv, tt, N, (int64_t)b * H + h, Npad, vs, vc, tile);
 }
 
 // ------------------------------------------------- Q, K and V in one call
@@ -654,72 +720,46 @@ __global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int6
 //      channel maximum and scale;
 //   3. per (64-token block, head, batch): the K codes and scale (smoothed) and
 //      the block's V codes.
-// ROPE: Q and K are replaced by their RMSNorm + RoPE transform as they are read
-// (the K block is transformed before it is summed and before its codes).
-template <bool ROPE>
-__global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, int N, int H, int64_t Npad,
-                                                        int nchunk, NormRope nr, int8_t *__restrict__ qc,
-                                                        float *__restrict__ qs, double *__restrict__ wsk,
-                                                        float *__restrict__ wsv) {
-    __shared__ float red[2][4];
-    __shared__ uint4 kbuf[kKBlock][kD / 8];      // the block's K rows, bf16 (16 KB)
-    __shared__ float vred[16][kD + 4];
-    const TokHead w = tok_head(H, (int)(Npad / 64));
-    const int tb = w.tb, h = w.h, b = w.b;
+// Per-channel max |V| over this thread's 4 raw rows, into vred[row] (16 rows of
+// partial maxima per workgroup; published by the caller's next barrier).
+__device__ __forceinline__ void v_block_max(const uint4 (&rv)[4], float (*vred)[kD + 4]) {
     const int t = threadIdx.x, row = t >> 4, seg = t & 15;
-    const int64_t bh = (int64_t)b * H + h;
-    // K and V rows (raw) of this thread: tokens row + 16 i; tokens >= N read as zero
-    const uint16_t *kb = k.data + (int64_t)b * k.sb + (int64_t)h * k.sh + seg * 8;
-    const uint16_t *vb = v.data + (int64_t)b * v.sb + (int64_t)h * v.sh + seg * 8;
     float vm[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int nt[4] = {tb * 64 + row, tb * 64 + row + 16, tb * 64 + row + 32, tb * 64 + row + 48};
-    if (ROPE) {
-        float xk[4][8];
-#pragma unroll
-        for (int i = 0; i < 4; i++) load_row8(kb + (int64_t)nt[i] * k.sn, nt[i] < N, xk[i]);
-        const float *gk[4] = {nr.gamma_k, nr.gamma_k, nr.gamma_k, nr.gamma_k};
-        uint4 y[4];
-        norm_rope_rows<4>(xk, gk, nt, nr, N, y);
-#pragma unroll
-        for (int i = 0; i < 4; i++) kbuf[row + 16 * i][seg] = y[i];
-    }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const int n = nt[i];
-        if (!ROPE) {
-            uint4 rk = make_uint4(0, 0, 0, 0);
-            if (n < N) rk = *reinterpret_cast<const uint4 *>(kb + (int64_t)n * k.sn);
-            kbuf[row + 16 * i][seg] = rk;
-        }
         float xv[8];
-        load_row8(vb + (int64_t)n * v.sn, n < N, xv);
+        widen8(rv[i], xv);
 #pragma unroll
         for (int j = 0; j < 8; j++) vm[j] = fmaxf(vm[j], fabsf(xv[j]));
     }
 #pragma unroll
     for (int j = 0; j < 8; j++) vred[row][seg * 8 + j] = vm[j];
-    float xq[4][8];
-    load_block(q, b, h, tb, N, xq);
-    if (ROPE) {
-        const float *gq[4] = {nr.gamma_q, nr.gamma_q, nr.gamma_q, nr.gamma_q};
-        uint4 y[4];
-        norm_rope_rows<4>(xq, gq, nt, nr, N, y);
-#pragma unroll
-        for (int i = 0; i < 4; i++) unpack_bf16x8(y[i], xq[i]);
-    }
+}
+
+// The two Q blocks' scales (workgroup maxima / 127) and codes of the 64-token
+// block held in xq (rows row + 16 i).
+__device__ __forceinline__ void q_codes_and_scales(const float (&xq)[4][8], int tb, int64_t bh, int64_t Npad,
+                                                   int8_t *__restrict__ qc, float *__restrict__ qs,
+                                                   float (*red)[4]) {
     float m[2];
     q_local_max(xq, m[0], m[1]);
-    block_maxes(m, red);                             // its barriers also publish kbuf and vred
+    block_maxes(m, red);
     const float sq0 = m[0] / 127.0f, sq1 = m[1] / 127.0f;
     store_int8_codes(xq, sq0, sq1, tb, bh, Npad, qc);
-    if (t == 0) {
+    if (threadIdx.x == 0) {
         qs[bh * (Npad / kQBlock) + 2 * tb] = sq0;
         qs[bh * (Npad / kQBlock) + 2 * tb + 1] = sq1;
     }
-    if (tb >= nchunk) return;                        // a padding block: zero Q codes only
+}
+
+// The block's chunk partials from LDS: threads 0..127 sum channel t of kbuf over
+// the 64 tokens in ascending order (fp64; zeros past N change no sum), threads
+// 128..255 reduce the 16 partial V maxima of channel t - 128.
+__device__ __forceinline__ void k_sum_v_max_partials(const uint4 (*kbuf)[kD / 8], const float (*vred)[kD + 4],
+                                                     int b, int tb, int h, int H, int nchunk,
+                                                     double *__restrict__ wsk, float *__restrict__ wsv) {
+    const int t = threadIdx.x;
     if (t < kD) {
-        // channel t summed over the block's tokens in ascending order (zeros past N
-        // change no fp64 sum)
         const uint16_t *col = reinterpret_cast<const uint16_t *>(&kbuf[0][0]) + t;
         double sum = 0.0;
 #pragma unroll 16
@@ -734,24 +774,105 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
     }
 }
 
+__global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, int N, int H, int64_t Npad,
+                                                        int nchunk, int8_t *__restrict__ qc, float *__restrict__ qs,
+                                                        double *__restrict__ wsk, float *__restrict__ wsv) {
+    __shared__ float red[2][4];
+    __shared__ uint4 kbuf[kKBlock][kD / 8];      // the block's K rows, bf16 (16 KB)
+    __shared__ float vred[16][kD + 4];
+    const TokHead w = tok_head(H, (int)(Npad / 64));
+    const int tb = w.tb, h = w.h, b = w.b;
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const int64_t bh = (int64_t)b * H + h;
+    // K, V and Q rows (raw) of this thread: tokens row + 16 i; tokens >= N read as
+    // zero.  Every load is in flight before any compute.
+    uint4 rk[4], rv[4], rq[4];
+    load_block_raw(k, b, h, tb, N, rk);
+    load_block_raw(v, b, h, tb, N, rv);
+    load_block_raw(q, b, h, tb, N, rq);
+    v_block_max(rv, vred);
+    float xq[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        kbuf[row + 16 * i][seg] = rk[i];
+        widen8(rq[i], xq[i]);
+    }
+    q_codes_and_scales(xq, tb, bh, Npad, qc, qs, red);   // its barriers also publish kbuf and vred
+    if (tb >= nchunk) return;                        // a padding block: zero Q codes only
+    k_sum_v_max_partials(kbuf, vred, b, tb, h, H, nchunk, wsk, wsv);
+}
+
+// The first pass with Q and K replaced by their RMSNorm + RoPE transform.  Two
+// workgroups per (64-token block, head, batch), adjacent in the logical grid: the
+// odd one transforms the Q block and writes its codes; the even one transforms
+// the K block (summed for k_mean; each row's norm factor r kept in kr for the
+// last pass, which then skips the sum of squares) and takes the V channel maxima.
+// Each holds half the rows of a combined workgroup, so more of them are resident.
+__global__ __launch_bounds__(256) void qkv_rope_pass1_kernel(View q, View k, View v, int N, int H, int64_t Npad,
+                                                             int nchunk, NormRope nr, int8_t *__restrict__ qc,
+                                                             float *__restrict__ qs, double *__restrict__ wsk,
+                                                             float *__restrict__ wsv, float *__restrict__ kr) {
+    __shared__ float red[2][4];
+    __shared__ uint4 kbuf[kKBlock][kD / 8];
+    __shared__ float vred[16][kD + 4];
+    const uint32_t id = xcd_remap(blockIdx.x, gridDim.x);
+    const uint32_t nblk = (uint32_t)(Npad / 64), lid = id >> 1;
+    const int tb = (int)((lid / (uint32_t)H) % nblk), h = (int)(lid % (uint32_t)H),
+              b = (int)(lid / ((uint32_t)H * nblk));
+    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
+    const int64_t bh = (int64_t)b * H + h;
+    const int n[4] = {tb * 64 + row, tb * 64 + row + 16, tb * 64 + row + 32, tb * 64 + row + 48};
+    uint4 y[4];
+    float r[4];
+    if (id & 1) {
+        uint4 rq[4];
+        load_block_raw(q, b, h, tb, N, rq);
+        norm_rope_rows<4>(rq, nr.gamma_q, nr.gamma_q, n, nr, N, y, r);
+        float xq[4][8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) widen8(y[i], xq[i]);
+        q_codes_and_scales(xq, tb, bh, Npad, qc, qs, red);
+        return;
+    }
+    uint4 rk[4], rv[4];
+    load_block_raw(k, b, h, tb, N, rk);
+    load_block_raw(v, b, h, tb, N, rv);
+    v_block_max(rv, vred);
+    norm_rope_rows<4>(rk, nr.gamma_k, nr.gamma_k, n, nr, N, y, r);
+    // the rows' norm factors: lane seg < 4 of each row group stores row seg's
+    // (token row + 16 seg), one store per wave
+    float rs = r[0];
+#pragma unroll
+    for (int i = 1; i < 4; i++) rs = seg == i ? r[i] : rs;
+    if (seg < 4) kr[bh * Npad + tb * 64 + row + 16 * seg] = rs;
+#pragma unroll
+    for (int i = 0; i < 4; i++) kbuf[row + 16 * i][seg] = y[i];
+    __syncthreads();                                 // publish kbuf and vred
+    if (tb >= nchunk) return;
+    k_sum_v_max_partials(kbuf, vred, b, tb, h, H, nchunk, wsk, wsv);
+}
+
 template <bool ROPE>
 __global__ __launch_bounds__(256) void qkv_pass3_kernel(View k, View v, int N, int H, int64_t Npad, NormRope nr,
                                                         const float *__restrict__ km, const float *__restrict__ vs,
-                                                        int8_t *__restrict__ kc, float *__restrict__ ks,
-                                                        uint8_t *__restrict__ vc) {
+                                                        const float *__restrict__ kr, int8_t *__restrict__ kc,
+                                                        float *__restrict__ ks, uint8_t *__restrict__ vc) {
     __shared__ float red[1][4];
     __shared__ uint32_t tile[kD][kTile / 4];
     const TokHead w = tok_head(H, (int)(Npad / 64));
     const int tb = w.tb, h = w.h, b = w.b;
     const int64_t bh = (int64_t)b * H + h;
+    uint4 rk[4], rv[4];                              // every row load in flight before any compute
+    load_block_raw(k, b, h, tb, N, rk);
+    load_v_tile_raw(v, b, h, tb, N, rv);
     float xk[4][8];
-    load_k_smoothed<ROPE>(k, b, h, tb, N, km, bh, nr, xk);
+    k_smoothed<ROPE>(rk, tb, N, km, bh, nr, kr, Npad, xk);
     float m[1] = {k_local_max(xk)};
     block_maxes(m, red);
     const float sk = m[0] / 127.0f;
     store_int8_codes(xk, sk, sk, tb, bh, Npad, kc);
     if (threadIdx.x == 0) ks[bh * (Npad / kKBlock) + tb] = sk;
-    v_tile_codes(v, b, h, tb, N, bh, Npad, vs, vc, tile);
+    v_tile_codes(rv, tb, N, bh, Npad, vs, vc, tile);
 }
 
 // ------------------------------------------------------------ launchers
@@ -788,7 +909,9 @@ hipError_t launch_quantize_v(View v, int B, int N, int H, uint8_t *vc, float *vs
     return hipSuccess;
 }
 
-// nr == nullptr: Q and K as given; otherwise their RMSNorm + RoPE transform.
+// nr == nullptr: Q and K as given; otherwise their RMSNorm + RoPE transform (the
+// workspace then also holds the K rows' norm factors, B * H * Npad floats, after
+// the amax block).
 hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, const NormRope *nr, int8_t *qc, float *qs,
                                int8_t *kc, float *ks, float *km, uint8_t *vc, float *vs, void *workspace,
                                hipStream_t stream) {
@@ -798,25 +921,26 @@ hipError_t launch_quantize_qkv(View q, View k, View v, int B, int N, int H, cons
     double *wsk = static_cast<double *>(workspace);
     float *wsv = reinterpret_cast<float *>(wsk + (int64_t)nchunk * total);
     float *amax = wsv + (int64_t)nchunk * total;
+    float *kr = nr ? amax + total : nullptr;
     const NormRope p = nr ? *nr : NormRope{};
     const dim3 grid((unsigned)(Npad / 64 * H * B));
     // passes 1 and 3 run over every 64-token block of the padded code buffers
     // (blocks past N write zero codes and scales); the partials exist for the
     // nchunk blocks that hold tokens
     if (nr)
-        LAUNCH_OR_RETURN(qkv_pass1_kernel<true>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
-                           wsk, wsv);
+        LAUNCH_OR_RETURN(qkv_rope_pass1_kernel, dim3(2 * grid.x), dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk,
+                           p, qc, qs, wsk, wsv, kr);
     else
-        LAUNCH_OR_RETURN(qkv_pass1_kernel<false>, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, p, qc, qs,
-                           wsk, wsv);
+        LAUNCH_OR_RETURN(qkv_pass1_kernel, grid, dim3(256), 0, stream, q, k, v, N, H, Npad, nchunk, qc, qs, wsk,
+                           wsv);
     LAUNCH_OR_RETURN((chunk_final_kernel<true, true>), final_grid(B, H), dim3(256), 0, stream, wsk, wsv, N, H,
                        nchunk, km, amax, vs);
     if (nr)
-        LAUNCH_OR_RETURN(qkv_pass3_kernel<true>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
-                           vc);
+        LAUNCH_OR_RETURN(qkv_pass3_kernel<true>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kr, kc,
+                           ks, vc);
     else
-        LAUNCH_OR_RETURN(qkv_pass3_kernel<false>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kc, ks,
-                           vc);
+        LAUNCH_OR_RETURN(qkv_pass3_kernel<false>, grid, dim3(256), 0, stream, k, v, N, H, Npad, p, km, vs, kr, kc,
+                           ks, vc);
     return hipSuccess;
 }
 

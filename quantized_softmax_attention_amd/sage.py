@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.sage_qk_workspace_bytes.argtypes, L.sage_qk_workspace_bytes.restype = [i, i, i, i], sz
         L.sage_v_workspace_bytes.argtypes, L.sage_v_workspace_bytes.restype = [i, i, i, i], sz
         L.sage_qkv_workspace_bytes.argtypes, L.sage_qkv_workspace_bytes.restype = [i, i, i, i], sz
+        L.sage_qkv_rope_workspace_bytes.argtypes, L.sage_qkv_rope_workspace_bytes.restype = [i, i, i, i], sz
         L.sage_quantize_qkv.argtypes = [pin, pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sage_quantize_qkv_noalloc.argtypes = [pin, pin, pin, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sage_qkv_noalloc_max_bytes.argtypes, L.sage_qkv_noalloc_max_bytes.restype = [], sz
@@ -215,6 +216,10 @@ def sage_quantize_v(v, v_codes, v_scale, workspace, stream=None) -> None:
 
 def sage_qkv_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
     return lib().sage_qkv_workspace_bytes(B, N, H, D)
+
+
+def sage_qkv_rope_workspace_bytes(B: int, N: int, H: int, D: int = HEAD_DIM) -> int:
+    return lib().sage_qkv_rope_workspace_bytes(B, N, H, D)
 
 
 def sage_quantize_qkv(q, k, v, q_codes, q_scale, k_codes, k_scale, k_mean, v_codes, v_scale, workspace,
@@ -395,7 +400,8 @@ class Buffers:
         self.v_scale = torch.empty(B, H, D, dtype=torch.float32, device=dev)
         self.ws_qk = torch.empty(max(1, sage_qk_workspace_bytes(B, N, H, D) // 8), dtype=torch.float64, device=dev)
         self.ws_v = torch.empty(max(1, sage_v_workspace_bytes(B, N, H, D) // 4), dtype=torch.float32, device=dev)
-        self.ws_qkv = torch.empty(max(1, sage_qkv_workspace_bytes(B, N, H, D) // 8), dtype=torch.float64,
+        # sized for sage_quantize_qkv_rope, which needs more than sage_quantize_qkv
+        self.ws_qkv = torch.empty(max(1, -(-sage_qkv_rope_workspace_bytes(B, N, H, D) // 8)), dtype=torch.float64,
                                   device=dev)
 
 

@@ -17,12 +17,12 @@ from quantized_softmax_attention_amd import inputs, sage  # noqa: E402
 EXPECTED = [
     ("sage_quantize_qk", ["kmean_partial_kernel", "chunk_final_kernel<true, false>", "quant_qk_kernel"]),
     ("sage_quantize_v", ["v_amax_partial_kernel", "chunk_final_kernel<false, true>", "quant_v_kernel"]),
-    ("sage_quantize_qkv", ["qkv_pass1_kernel<false>", "chunk_final_kernel<true, true>", "qkv_pass3_kernel<false>"]),
+    ("sage_quantize_qkv", ["qkv_pass1_kernel", "chunk_final_kernel<true, true>", "qkv_pass3_kernel<false>"]),
     ("sage_attn_fwd", ["attn_i8f8_kernel<-1>"]),
     ("sage_attn_fwd_bf16", ["attn_bf16_kernel"]),
     ("sage_attn_fwd_int8qk", ["attn_int8qk_kernel"]),
     ("sage_qk_norm_rope", ["norm_rope_kernel"]),
-    ("sage_quantize_qkv_rope", ["qkv_pass1_kernel<true>", "chunk_final_kernel<true, true>",
+    ("sage_quantize_qkv_rope", ["qkv_rope_pass1_kernel", "chunk_final_kernel<true, true>",
                                 "qkv_pass3_kernel<true>"]),
     ("sage_mx_quantize", ["mx_quantize_kernel<0>"]),
     ("sage_attn_fwd_mx", ["attn_i8f8_kernel<0>"]),

@@ -68,6 +68,10 @@ def test_quantize_qk_validation():
     assert qk(q=view(data=None)) == NULL
     assert qk(Dv=64) == SHAPE and qk(Nv=0) == SHAPE and qk(Bv=0) == SHAPE and qk(Hv=0) == SHAPE
     assert qk(Hv=70000) == SHAPE
+    # every launch's work-items (at most 8 B H Npad) fit 32 bits: B H Npad <= 2^29 - 1
+    assert sage.sage_qkv_workspace_bytes(1, (1 << 28) - 256, 2, D) > 0     # Npad = 2^28 - 256: fits
+    assert sage.sage_qkv_workspace_bytes(1, (1 << 28) - 255, 2, D) == 0    # Npad = 2^28: 8 B H Npad = 2^32
+    assert qk(Bv=1, Hv=2, Nv=(1 << 28) - 255) == SHAPE
     assert qk(q=view(data=A + 8)) == ALIGN
     assert qk(q=view(sn=3 * H * D + 4)) == ALIGN
     assert qk(ptrs=(A + 4, A, A, A, A)) == ALIGN
@@ -218,7 +222,9 @@ def test_qk_norm_rope_validation():
 
 def test_quantize_qkv_rope_validation():
     L = sage.lib()
-    wsb = sage.sage_qkv_workspace_bytes(B, N, H, D)
+    wsb = sage.sage_qkv_rope_workspace_bytes(B, N, H, D)
+    # the qkv workspace plus one fp32 norm factor per (b, h, padded token)
+    assert wsb == sage.sage_qkv_workspace_bytes(B, N, H, D) + B * H * sage.sage_npad(N) * 4
     call = lambda g=(A, A, A), eps=1e-6, ptrs=(A,) * 7, ws=A, w=wsb, Dv=D: L.sage_quantize_qkv_rope(
         ctypes.byref(view()), ctypes.byref(view(A + 2 * H * D)), ctypes.byref(view(A + 4 * H * D)), B, N, H, Dv,
         *g, eps, *ptrs, ws, w, None)
@@ -229,6 +235,7 @@ def test_quantize_qkv_rope_validation():
     assert call(ptrs=(A + 8, A, A, A, A, A, A)) == ALIGN
     assert call(eps=float("inf")) == VALUE
     assert call(w=wsb - 8) == WORKSPACE
+    assert call(w=sage.sage_qkv_workspace_bytes(B, N, H, D)) == WORKSPACE   # the qkv size is not enough
 
 
 @pytest.mark.parametrize("lang,std", [("c", "-std=c99"), ("c++", "-std=c++11")])
