@@ -13,21 +13,27 @@ Prints ONE JSON line.  Besides the contract keys it carries:
   roofline      -- the attention kernel (dominant) against the INT8/FP8 MFMA peak;
                    its duration is measured with HIP events on its own stream.
   stages        -- per-stage ms and the quantisers' achieved HBM bandwidth.
-  bf16_path     -- the unquantised BF16-MFMA path on the same inputs.
-  int8qk_path   -- INT8 Q K^T with the bf16 V unquantised (BF16 P.V) on the same inputs.
+  bf16_path     -- the unquantised BF16-MFMA path on the same inputs (output
+                   digest; with the CPU leg, rel-L2 against the exact fp64 result
+                   on 64 sampled rows per head, gate 5e-3).
+  int8qk_path   -- INT8 Q K^T with the bf16 V unquantised (BF16 P.V) on the same inputs
+                   (output digest; with the CPU leg, rel-L2 against its oracle,
+                   gate 1e-3).
   rope_path     -- RMSNorm + RoPE of Q and K before quantisation: in place
                    (sage_qk_norm_rope) then sage_quantize_qkv, against the fused
-                   sage_quantize_qkv_rope (same codes, Q and K never written).
+                   sage_quantize_qkv_rope (Q and K never written); both sets of
+                   codes and scales digested, byte_exact when they are equal.
   mx_path       -- the attention with its output written as OCP MX blocks (E4M3 and
                    E2M1) by the fused epilogue, against attention + the standalone
-                   MX quantiser (sage_mx_quantize) on the bf16 output.
+                   MX quantiser (sage_mx_quantize) on the bf16 output; both
+                   digested, byte_exact when equal.
   cpu_baseline  -- the CPU oracle (quantisers in full + step-by-step quantised
                    attention on sampled rows, extrapolated), on the host cores.
   parity        -- the timed output at those sampled rows against the oracle's
                    result (rounded to bf16): whole-set rel-L2 and the largest
                    row error against the typical row norm (plus each row's
-                   error against its own norm, and the worst rows); the run
-                   exits non-zero above the gates.
+                   error against its own norm, and the worst rows).  The run
+                   exits non-zero above any gate or when a byte-exact pair differs.
   output_sha256 -- digest of the timed output's bytes.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--copy-calibration]
@@ -181,6 +187,41 @@ def cpu_baseline(case, rows_per_head=512, heads=None):
     }
 
 
+def tensor_sha256(*ts) -> str:
+    """sha256 of the raw bytes of the given tensors, in order."""
+    import torch  # noqa: F401  (the tensors' own module; imported where the GPU work is)
+
+    h = hashlib.sha256()
+    for t in ts:
+        h.update(t.detach().contiguous().view(-1).view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def out_rows(out, rows):
+    """A token-major bf16 output [B, N, H*D] (on the GPU) at sampled rows [B, H', R] -> fp64 [B, H', R, D]."""
+    import numpy as np
+    import torch
+
+    Bq, Hq, R = rows.shape
+    o = out.view(out.shape[0], out.shape[1], -1, D)[:, :, :Hq]            # [B, N, H', D]
+    idx = torch.from_numpy(np.ascontiguousarray(rows.transpose(0, 2, 1))).long().to(out.device)   # [B, R, H']
+    got = torch.gather(o, 1, idx[..., None].expand(Bq, R, Hq, D)).float().cpu().numpy()
+    return got.transpose(0, 2, 1, 3).astype(np.float64)                     # [B, H', R, D]
+
+
+def row_errors(got, ref):
+    """Whole-set rel-L2 and per-row errors of got against ref ([..., D] fp64): each row's L2 error over the
+    RMS row norm of ref (the per-row bound) and over its own norm."""
+    import numpy as np
+
+    err = np.sqrt(((got - ref) ** 2).sum(-1))
+    nrm = np.sqrt((ref ** 2).sum(-1))
+    typical = float(np.sqrt((nrm ** 2).mean()))
+    return {"rel_l2": float(np.sqrt((err ** 2).sum() / (nrm ** 2).sum())),
+            "max_row_err_vs_typical_row": float(err.max() / typical),
+            "max_row_rel_l2": float((err / np.maximum(nrm, 1e-300)).max())}
+
+
 def parity_vs_method(out, rows, meth):
     """The timed bf16 output [B, N, H*D] (token-major, on the GPU) at the oracle's sampled rows [B, H', R]
     against the step-by-step quantised oracle's result there [B, H', R, D], rounded to bf16 as the kernel
@@ -189,10 +230,7 @@ def parity_vs_method(out, rows, meth):
     import torch
 
     Bq, Hq, R = rows.shape
-    o = out.view(out.shape[0], out.shape[1], -1, D)[:, :, :Hq]            # [B, N, H', D]
-    idx = torch.from_numpy(np.ascontiguousarray(rows.transpose(0, 2, 1))).long().to(out.device)   # [B, R, H']
-    got = torch.gather(o, 1, idx[..., None].expand(Bq, R, Hq, D)).float().cpu().numpy()
-    got = got.transpose(0, 2, 1, 3).astype(np.float64)                      # [B, H', R, D]
+    got = out_rows(out, rows)
     ref = torch.from_numpy(meth).float().to(torch.bfloat16).double().numpy()
     err = np.sqrt(((got - ref) ** 2).sum(-1))
     nrm = np.sqrt((ref ** 2).sum(-1))
@@ -207,6 +245,33 @@ def parity_vs_method(out, rows, meth):
                            for i in worst],
             "rows": int(Bq * Hq * R), "reference": "step-by-step quantised oracle, rounded to bf16",
             "gate": {"rel_l2_vs_method": PARITY_GATE, "max_row_err_vs_typical_row": PARITY_ROW_GATE}}
+
+
+SIDE_GATES = {"bf16_path": 5e-3, "int8qk_path": 1e-3}   # rel-L2, as the GPU tests; rows: PARITY_ROW_GATE
+
+
+def side_parity(case, codes, rows, got16, gotq):
+    """The bf16 path's output at the sampled rows against the exact fp64 result, and the INT8-QK / bf16-PV
+    path's against the step-by-step oracle of the same precision split rounded to bf16 (the GPU tests'
+    references and gates)."""
+    import torch
+
+    import oracle
+    from tests.helpers import oracle_view
+
+    q, k, v = (oracle_view(t) for t in (case.q, case.k, case.v))
+    qc, qs, kc, ks = codes
+    sm = 1.0 / math.sqrt(D)
+    exact = oracle.attn_exact(q, k, v, sm, rows)
+    meth = oracle.attn_int8qk(qc, qs, kc, ks, v, sm, rows)
+    meth16 = torch.from_numpy(meth).float().to(torch.bfloat16).double().numpy()
+    res = {"bf16_path": {**row_errors(got16, exact), "reference": "exact fp64 attention"},
+           "int8qk_path": {**row_errors(gotq, meth16), "reference": "step-by-step INT8-QK / bf16-PV oracle, bf16"}}
+    for name, r in res.items():
+        r["rows"] = int(rows.size)
+        r["gate"] = {"rel_l2": SIDE_GATES[name], "max_row_err_vs_typical_row": PARITY_ROW_GATE}
+        r["ok"] = r["rel_l2"] <= SIDE_GATES[name] and r["max_row_err_vs_typical_row"] <= PARITY_ROW_GATE
+    return res
 
 
 def rescale_fraction(codes, N, H, waves_per_head=4, head_step=7):
@@ -477,6 +542,8 @@ def main():
         e[1].record(stream)
     stream.synchronize()
     bf16_ms = [e[0].elapsed_time(e[1]) for e in e16]
+    side_rows = inputs.sample_rows(B, H, N, count=64, tail=16)        # rows checked against the oracle
+    bf16_sha, got16 = tensor_sha256(out16), out_rows(out16, side_rows)
 
     # INT8 Q K^T with the bf16 V unquantised (codes of the last step's quantise_qk)
     eq = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.bf16_calls)]
@@ -487,13 +554,16 @@ def main():
         e[1].record(stream)
     stream.synchronize()
     int8qk_ms = [e[0].elapsed_time(e[1]) for e in eq]
+    int8qk_sha, gotq = tensor_sha256(out16), out_rows(out16, side_rows)
+    del out16
 
     # RMSNorm + RoPE of Q and K: in place then quantise, vs fused into the quantiser
     nr = inputs.norm_rope_params(N).to(dev)
     pk = g.packed.clone()                 # the in-place transform works on a copy
     HD = H * D
     pq, pk_k = (pk[:, :, i * HD:(i + 1) * HD].unflatten(2, (H, D)) for i in range(2))
-    rbuf = sage.Buffers(B, N, H, device=dev)
+    rbuf = sage.Buffers(B, N, H, device=dev)              # fused
+    ubuf = sage.Buffers(B, N, H, device=dev)              # in place, then sage_quantize_qkv
     er = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.bf16_calls)]
     sage.quantize_qkv_rope(g.q, g.k, g.v, nr, rbuf, stream)
     for e in er:
@@ -504,11 +574,13 @@ def main():
         e[0].record(stream)
         sage.sage_qk_norm_rope(pq, pk_k, nr.gamma_q, nr.gamma_k, nr.rope, nr.eps, stream)
         e[1].record(stream)
-        sage.quantize_qkv(pq, pk_k, g.v, rbuf, stream)
+        sage.quantize_qkv(pq, pk_k, g.v, ubuf, stream)
         e[2].record(stream)
         sage.quantize_qkv_rope(g.q, g.k, g.v, nr, rbuf, stream)
         e[3].record(stream)
     stream.synchronize()
+    codes_of = lambda bb: (bb.q_codes, bb.q_scale, bb.k_codes, bb.k_scale, bb.k_mean, bb.v_codes, bb.v_scale)
+    rope_sha, unf_sha = tensor_sha256(*codes_of(rbuf)), tensor_sha256(*codes_of(ubuf))
     nr_ms = [e[0].elapsed_time(e[1]) for e in er]
     unf_ms = [e[0].elapsed_time(e[2]) for e in er]
     fused_ms = [e[2].elapsed_time(e[3]) for e in er]
@@ -518,13 +590,15 @@ def main():
             "unfused_norm_rope_plus_qkv_ms": stats_ms(unf_ms),
             "qkv_rope_fused_ms": stats_ms(fused_ms),
             "qkv_rope_fused_GBps": rb["qkv_rope"] / (statistics.fmean(fused_ms) * 1e-3) / 1e9,
+            "codes_sha256": rope_sha, "unfused_codes_sha256": unf_sha, "byte_exact": rope_sha == unf_sha,
             "pages_context": {"gb10_block24_rms_rope_p50_ms": 12.535, "note": "NVIDIA GB10, whole rms_rope component"}}
-    del pk, rbuf
+    del pk, rbuf, ubuf
 
     # MX output: fused epilogue vs the standalone quantiser over the bf16 output
     mx = {}
     for fmt, name in ((sage.MX_E4M3, "e4m3"), (sage.MX_E2M1, "e2m1")):
-        codes, scales = sage.mx_out(B, N, H, fmt, device=dev)
+        codes, scales = sage.mx_out(B, N, H, fmt, device=dev)       # fused epilogue
+        codes_s, scales_s = sage.mx_out(B, N, H, fmt, device=dev)   # standalone quantiser over `out`
         ef = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.bf16_calls)]
         sage.sage_attn_fwd_mx(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, fmt,
                               codes, scales, sm, stream)
@@ -533,7 +607,7 @@ def main():
             sage.sage_attn_fwd_mx(buf.q_codes, buf.q_scale, buf.k_codes, buf.k_scale, buf.v_codes, buf.v_scale, fmt,
                                   codes, scales, sm, stream)
             e[1].record(stream)
-            sage.sage_mx_quantize(out, fmt, codes, scales, stream)
+            sage.sage_mx_quantize(out, fmt, codes_s, scales_s, stream)
             e[2].record(stream)
         stream.synchronize()
         fused = [e[0].elapsed_time(e[1]) for e in ef]
@@ -544,7 +618,10 @@ def main():
                     "mx_quantize_ms": stats_ms(alone),
                     "mx_quantize_GBps": mx_bytes / (statistics.fmean(alone) * 1e-3) / 1e9,
                     "unfused_ms": attn_mean + statistics.fmean(alone)}
-        del codes, scales
+        mx[name]["output_sha256"] = tensor_sha256(codes, scales)
+        mx[name]["unfused_sha256"] = tensor_sha256(codes_s, scales_s)
+        mx[name]["byte_exact"] = mx[name]["output_sha256"] == mx[name]["unfused_sha256"]
+        del codes, scales, codes_s, scales_s
 
     # one GPU's share of an 8-way head split: 7 heads of the same buffer (strided
     # views of their columns), writing their slice of the token-major output
@@ -635,10 +712,10 @@ def main():
             "attn_pct_of_i8f8_peak": 100.0 * achieved / PEAK_I8F8_TFLOPS,
             "step_pct_of_i8f8_peak": 100.0 * value / PEAK_I8F8_TFLOPS,
         },
-        "bf16_path": {"ms_per_call": stats_ms(bf16_ms),
+        "bf16_path": {"ms_per_call": stats_ms(bf16_ms), "output_sha256": bf16_sha,
                       "tflops": flops / (statistics.fmean(bf16_ms) * 1e-3) / 1e12,
                       "frac_of_bf16_peak": flops / (statistics.fmean(bf16_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
-        "int8qk_path": {"ms_per_call": stats_ms(int8qk_ms),
+        "int8qk_path": {"ms_per_call": stats_ms(int8qk_ms), "output_sha256": int8qk_sha,
                         "tflops": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12,
                         "frac_of_peak": flops / (statistics.fmean(int8qk_ms) * 1e-3) / 1e12 / PEAK_INT8QK_TFLOPS,
                         "peak_note": "half the ops at the INT8 peak, half at the BF16 peak: 1/(0.5/5000 + 0.5/2500)"},
@@ -651,12 +728,17 @@ def main():
         "input_generation_s": gen_s,
     }
     line["output_sha256"] = out_sha
-    ok = True
+    # the byte-exact pairs: fused vs unfused RoPE quantiser, fused vs standalone MX quantiser
+    ok = rope["byte_exact"] and all(m["byte_exact"] for m in mx.values())
     if not args.no_cpu:
         extras, line["cpu_baseline"] = cpu_baseline(case)
         par = parity_vs_method(out, extras["rows"], extras["method"])
         line["parity"] = par
-        ok = par["rel_l2_vs_method"] <= PARITY_GATE and par["max_row_err_vs_typical_row"] <= PARITY_ROW_GATE
+        ok = ok and par["rel_l2_vs_method"] <= PARITY_GATE and par["max_row_err_vs_typical_row"] <= PARITY_ROW_GATE
+        side = side_parity(case, extras["codes"], side_rows, got16, gotq)
+        for name, r in side.items():
+            line[name]["parity"] = r
+            ok = ok and r["ok"]
         # VALU roofline of the attention kernel: the issue floor of its instruction stream (tile replay) at
         # the workload's share of rescaling tiles, over the measured kernel time at the measured clock
         frac = rescale_fraction(extras["codes"], N, H)
@@ -674,7 +756,8 @@ def main():
         line["parity"] = None
     print(json.dumps(line), flush=True)
     if not ok:
-        print("bench.py: the timed output is not within the parity gate of the quantised oracle", file=sys.stderr)
+        print("bench.py: a timed output failed its check (parity gate of an oracle, or a byte-exact pair)",
+              file=sys.stderr)
         sys.exit(1)
 
 

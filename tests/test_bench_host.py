@@ -98,3 +98,46 @@ def test_rescale_fraction_counts_moved_maxima():
     _, (qc, qs, kc, ks, _, _) = _tiny_oracle()
     f = bench.rescale_fraction((qc, qs, kc, ks), 256, 2, waves_per_head=4, head_step=1)
     assert 0.0 < f <= 1.0
+
+
+def test_side_parity_passes_the_oracles_own_rows_and_catches_a_wrong_row():
+    # the bench's check of the bf16 and INT8-QK paths, fed the oracle's own results (as a correct kernel's
+    # would be, up to rounding) passes; one row replaced by another row's values fails its per-row bound
+    import numpy as np
+    import torch
+
+    import oracle
+    from quantized_softmax_attention_amd import inputs
+    from tests.helpers import oracle_view
+
+    case = inputs.packed_case(1, 300, 2, seed=77)
+    q, k, v = (oracle_view(t) for t in (case.q, case.k, case.v))
+    km = oracle.kmean(k)
+    (qc, qs), (kc, ks) = oracle.quant_q(q, 32), oracle.quant_k(k, km, 64)
+    rows = inputs.sample_rows(1, 2, 300, count=40, tail=8)
+    sm = 1.0 / np.sqrt(128.0)
+    exact = oracle.attn_exact(q, k, v, sm, rows)
+    meth = torch.from_numpy(oracle.attn_int8qk(qc, qs, kc, ks, v, sm, rows)).float().to(torch.bfloat16).double()
+    got16 = torch.from_numpy(exact).float().to(torch.bfloat16).double().numpy()
+    res = bench.side_parity(case, (qc, qs, kc, ks), rows, got16, meth.numpy())
+    assert res["bf16_path"]["ok"] and res["int8qk_path"]["ok"]
+    assert res["bf16_path"]["rel_l2"] < 5e-3 and res["int8qk_path"]["rel_l2"] == 0.0
+    bad = meth.numpy().copy()
+    bad[0, 1, 3] = bad[0, 1, 4]
+    res = bench.side_parity(case, (qc, qs, kc, ks), rows, got16, bad)
+    assert not res["int8qk_path"]["ok"] and res["int8qk_path"]["max_row_err_vs_typical_row"] > 3e-2
+
+
+def test_out_rows_gathers_token_major_rows():
+    import numpy as np
+    import torch
+
+    B, N, H, D = 2, 5, 3, 128
+    out = torch.arange(B * N * H * D, dtype=torch.float32).reshape(B, N, H * D).to(torch.bfloat16)
+    rows = np.array([[[4, 0], [1, 1], [2, 3]], [[0, 0], [3, 2], [4, 4]]], dtype=np.int32)   # [B, H, R]
+    got = bench.out_rows(out, rows)
+    for b in range(B):
+        for h in range(H):
+            for r in range(2):
+                n = rows[b, h, r]
+                assert np.array_equal(got[b, h, r], out[b, n, h * D:(h + 1) * D].double().numpy())
