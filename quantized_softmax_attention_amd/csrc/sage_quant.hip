@@ -235,7 +235,8 @@ __device__ uint32_t sq_words_to_f32(const uint32_t *w) {
 
 // The slow path for one row group (all 16 of its lanes active, 8 values each);
 // a call, not inlined per row: it is rare, and its code would otherwise repeat
-// in every row of every kernel that normalises.
+// in every row of every kernel that normalises.  The row is passed by value
+// (registers): an array reference would put it in scratch memory for the call.
 struct Row8 {
     float v[8];
 };
@@ -720,6 +721,10 @@ __global__ __launch_bounds__(256) void quant_v_kernel(View v, int N, int H, int6
 //      channel maximum and scale;
 //   3. per (64-token block, head, batch): the K codes and scale (smoothed) and
 //      the block's V codes.
+// With the RMSNorm + RoPE transform (qkv_rope_pass1_kernel, qkv_pass3_kernel<true>),
+// Q and K are replaced by their transform as they are read: the K block is
+// transformed before it is summed and before its codes.
+
 // Per-channel max |V| over this thread's 4 raw rows, into vred[row] (16 rows of
 // partial maxima per workgroup; published by the caller's next barrier).
 __device__ __forceinline__ void v_block_max(const uint4 (&rv)[4], float (*vred)[kD + 4]) {
