@@ -102,6 +102,13 @@ def attn_bytes(b=B, n=N, h=H, d=D) -> int:
     return 3 * b * h * npad * d + 2 * b * n * h * d
 
 
+def kv_restream_bytes(b=B, n=N, h=H, d=D, queries_per_workgroup=128) -> int:
+    """On-chip secondary bound of the attention: every workgroup (one block of 128 queries of one head) stages
+    its head's whole K and V codes (padded) from L2 into LDS."""
+    npad = (n + 255) // 256 * 256
+    return -(-n // queries_per_workgroup) * 2 * npad * d * h * b
+
+
 CSRC = os.path.join(ROOT, "quantized_softmax_attention_amd", "csrc")
 # the sources the fused attention kernel is compiled from
 ATTN_SOURCES = [os.path.join(CSRC, f) for f in ("sage_attn.hip", "sage_attn_parts.h", "sage_common.h")]
@@ -699,12 +706,17 @@ def main():
                      "sclk_mhz_measured": sclk,
                      "peak_at_measured_sclk": None if sclk is None else 256 * 8192 * sclk * 1e6 / 1e12,
                      "frac_at_measured_sclk": None if sclk is None else achieved / (256 * 8192 * sclk * 1e6 / 1e12),
-                     "peak_note": "5000 = published dense INT8/FP8 figure; 256 CU x 8192 ops/clk x 2.4 GHz = 5033"},
+                     "peak_note": "5000 = published dense INT8/FP8 figure; 256 CU x 8192 ops/clk x 2.4 GHz = 5033",
+                     # on-chip: the K/V codes every workgroup stages from L2 into LDS, and that rate
+                     "kv_restream_bytes_per_launch": kv_restream_bytes(),
+                     "kv_restream_GBps": kv_restream_bytes() / (attn_mean * 1e-3) / 1e9},
         "attn_rounds": {"all": stats_ms(all_round_ms), "rounds": rounds, "sensor_note": sensors.note},
         "stages": {
             "qkv_quantize_ms": stats_ms(qkv_ms), "attn_fwd_ms": stats_ms(at_ms), "step_ms_events": stats_ms(step_ms),
             "qkv_quantize_GBps": (qb["qk_quantize"] + qb["v_quantize"]) / (statistics.fmean(qkv_ms) * 1e-3) / 1e9,
             "qk_quantize_ms": stats_ms(qk_ms), "v_quantize_ms": stats_ms(v_ms),
+            # the pages' pipeline: the two quantiser calls then the attention (means of the separate timings)
+            "pipeline_qk_v_attn_ms": statistics.fmean(qk_ms) + statistics.fmean(v_ms) + attn_mean,
             "qk_quantize_GBps": qb["qk_quantize"] / (statistics.fmean(qk_ms) * 1e-3) / 1e9,
             "v_quantize_GBps": qb["v_quantize"] / (statistics.fmean(v_ms) * 1e-3) / 1e9,
             "hbm_peak_GBps": PEAK_HBM_GBS,

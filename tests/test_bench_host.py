@@ -27,6 +27,8 @@ def test_algorithmic_counts():
     e = N * H * D
     assert q["qk_quantize"] == 6 * e + 2 * H * npad * D
     assert q["v_quantize"] == 4 * e + H * npad * D
+    # every 128-query block of every head stages its head's padded K and V codes into LDS once
+    assert bench.kv_restream_bytes() == 296 * 2 * npad * D * H == 160_776_060_928
     r = bench.rope_bytes()
     assert r["norm_rope"] == 8 * e + N * D * 4
     assert r["qkv_rope"] == q["qk_quantize"] + q["v_quantize"] + 2 * N * D * 4
