@@ -459,12 +459,11 @@ __device__ __forceinline__ float div_rn(float x, float scale, float inv) {
     return __builtin_copysignf(__builtin_fmaf(r, inv, q0), x);
 }
 
-// INT8 code of x / scale: ties to even, clamped to [-127, 127]; 0 when scale is 0.
-// FAST: scale >= kFastDivMin and inv = 1.0f / scale.
-template <bool FAST>
-__device__ __forceinline__ uint32_t int8_code(float x, float scale, float inv) {
+// INT8 code of x / scale (IEEE division): ties to even, clamped to [-127, 127]; 0
+// when scale is 0.  The path for blocks whose scale is below kFastDivMin.
+__device__ __forceinline__ uint32_t int8_code(float x, float scale) {
     if (scale == 0.0f) return 0u;
-    float r = __builtin_rintf(FAST ? div_rn(x, scale, inv) : x / scale);
+    float r = __builtin_rintf(x / scale);
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (uint32_t)((int32_t)r) & 0xFFu;
 }
@@ -508,6 +507,19 @@ __device__ __forceinline__ float k_local_max(const float (&x)[4][8]) {
     return m;
 }
 
+// The INT8 code of x / scale for a block scale scale = RN(m / 127) >= kFastDivMin,
+// m the largest |x| of the block, in the low byte of the result.  Then
+// |x / scale| <= 127 (1 + 2^-24), so the correctly rounded quotient q rounds to an
+// integer in [-127, 127] (no clamp), and q + 1.5 * 2^23 lies in [2^23, 2^24),
+// where fp32 values are the integers: that one addition rounds q to nearest even,
+// and the sum is rint(q) + 1.5 * 2^23, whose low byte is rint(q) in two's
+// complement.  (The sign of a zero quotient does not matter: both give code 0.)
+__device__ __forceinline__ uint32_t int8_code_fast(float x, float scale, float inv) {
+    const float q0 = x * inv;
+    const float q = __builtin_fmaf(__builtin_fmaf(-q0, scale, x), inv, q0);
+    return __float_as_uint(q + 0x1.8p23f);
+}
+
 // Codes of the thread's 4 x 8 values with scale sc(i) for token row i.
 template <bool FAST>
 __device__ __forceinline__ void store_int8_codes_as(const float (&x)[4][8], float s_lo, float s_hi, int tb,
@@ -519,7 +531,9 @@ __device__ __forceinline__ void store_int8_codes_as(const float (&x)[4][8], floa
         const float sc = i < 2 ? s_lo : s_hi, inv = i < 2 ? i_lo : i_hi;
         uint32_t c[2] = {0, 0};
 #pragma unroll
-        for (int j = 0; j < 8; j++) c[j >> 2] |= int8_code<FAST>(x[i][j], sc, inv) << (8 * (j & 3));
+        for (int j = 0; j < 8; j++)
+            c[j >> 2] |= (FAST ? int8_code_fast(x[i][j], sc, inv) & 0xFFu : int8_code(x[i][j], sc))
+                         << (8 * (j & 3));
         const int64_t off = (bh * Npad + (int64_t)tb * 64 + row + 16 * i) * kD + seg * 8;
         *reinterpret_cast<uint2 *>(codes + off) = make_uint2(c[0], c[1]);
     }
@@ -670,15 +684,20 @@ __device__ __forceinline__ void v_tile_codes(const uint4 (&raw)[4], int tt, int 
 #pragma unroll
     for (int j = 0; j < 8; j++) fast = fast && sv[j] >= kFastDivMin;
     if (fast) {
+        // sv = RN(amax / 448) is normal here, so every quotient has |y| <= 448 (1 + 2^-23):
+        // no saturation, and the conversion instruction rounds it as the E4M3 codec does
+        // (checked against the codec over that range, both zeros and fp32 subnormals,
+        // by the instruction probe tests).  Keys 4g, 4g + 1 fill bytes 0, 1 and keys
+        // 4g + 2, 4g + 3 bytes 2, 3.  Rows past N were loaded as +0: their codes are 0.
         float inv[8];
 #pragma unroll
         for (int j = 0; j < 8; j++) inv[j] = 1.0f / sv[j];
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int n = tt * kTile + 4 * g + i;
-#pragma unroll
-            for (int j = 0; j < 8; j++)
-                packed[j] |= (n >= N ? 0u : e4m3_encode(div_rn(x[i][j], sv[j], inv[j]))) << (8 * i);
+        for (int j = 0; j < 8; j++) {
+            const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(div_rn(x[0][j], sv[j], inv[j]),
+                                                          div_rn(x[1][j], sv[j], inv[j]), 0, false);
+            packed[j] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(div_rn(x[2][j], sv[j], inv[j]),
+                                                                  div_rn(x[3][j], sv[j], inv[j]), lo, true);
         }
     } else {
 #pragma unroll

@@ -7,7 +7,8 @@
   aligned to the group's largest product with about 12 fractional bits (smaller
   terms are truncated); the group sums and the input accumulator are added in
   fp32.  Measured: |error| <= 2^-10 of the largest product of a dot product.
-* v_cvt_pk_fp8_f32 rounds like the oracle's E4M3FN codec on [0, 460].
+* v_cvt_pk_fp8_f32 rounds like the oracle's E4M3FN codec on [0, 460], and on [-448.0001, 448.0001]
+  with both zeros and fp32 subnormals (the V quantiser's quotients).
 * v_permlane32_swap(x, x) gives each lane the values of lanes l%32 and l%32 + 32.
 * v_exp_f32 is exact at integers and within a few ulp elsewhere.
 """
@@ -140,6 +141,30 @@ def test_cvt_pk_fp8_matches_codec(probe):
     x = np.concatenate([table, mids, rng.uniform(0, 448, 100000), np.exp(rng.uniform(-12, np.log(448), 100000)),
                         [448.0, 448.001, 450.0, 455.0, 459.9, 2.0 ** -10, 3 * 2.0 ** -11, 0.0]]).astype(np.float32)
     x = np.concatenate([x, np.zeros((-len(x)) % 4, np.float32)])
+    tx = torch.from_numpy(x).cuda()
+    out = torch.zeros(len(x), dtype=torch.uint8, device="cuda")
+    assert probe.sage_probe_cvt_fp8(ctypes.c_void_p(tx.data_ptr()), len(x), ctypes.c_void_p(out.data_ptr())) == 0
+    got = out.cpu().numpy()
+    want = oracle.e4m3_encode(x)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float(x[i]), int(got[i]), int(want[i])) for i in bad[:10]]
+
+
+def test_cvt_pk_fp8_matches_codec_signed_and_tiny(probe):
+    """The V quantiser's quotients: |y| <= 448 (1 + 2^-22) of either sign, both zeros, every
+    rounding boundary and its fp32 neighbours, magnitudes down to the fp32 subnormals."""
+    table = oracle.e4m3_decode(np.arange(0x7F)).astype(np.float32)
+    mids = ((table[1:].astype(np.float64) + table[:-1]) / 2).astype(np.float32)   # exact in fp32
+    rng = np.random.default_rng(6)
+    mags = np.concatenate([
+        table, mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(np.inf)),
+        rng.uniform(0, 448, 100000).astype(np.float32),
+        np.exp2(rng.uniform(-150, np.log2(448), 200000)).astype(np.float32),   # to the fp32 subnormals
+        np.array([448.0, np.nextafter(np.float32(448), np.float32(np.inf)), 448 * (1 + 2.0 ** -22), 2.0 ** -10,
+                  2.0 ** -126, 2.0 ** -149, 3 * 2.0 ** -149, 2.0 ** -127], np.float32)])
+    x = np.concatenate([mags, -mags]).astype(np.float32)
+    x = np.concatenate([x, np.zeros((-len(x)) % 4, np.float32)])
+    assert np.signbit(x).any() and (x == 0).any() and (np.abs(x[x != 0]) < 2.0 ** -126).any()
     tx = torch.from_numpy(x).cuda()
     out = torch.zeros(len(x), dtype=torch.uint8, device="cuda")
     assert probe.sage_probe_cvt_fp8(ctypes.c_void_p(tx.data_ptr()), len(x), ctypes.c_void_p(out.data_ptr())) == 0
