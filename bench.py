@@ -398,6 +398,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--bf16-calls", type=int, default=5,
                     help="timed calls of each comparison path (bf16, INT8-QK/bf16-PV)")
+    ap.add_argument("--rope-calls", type=int, default=20,
+                    help="timed rounds of the RMSNorm + RoPE comparison (about 2.5 ms each)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle cpu_baseline leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also launch one plain 1 GiB device copy (for HBM counter scaling)")
@@ -571,7 +573,7 @@ def main():
     pq, pk_k = (pk[:, :, i * HD:(i + 1) * HD].unflatten(2, (H, D)) for i in range(2))
     rbuf = sage.Buffers(B, N, H, device=dev)              # fused
     ubuf = sage.Buffers(B, N, H, device=dev)              # in place, then sage_quantize_qkv
-    er = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.bf16_calls)]
+    er = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.rope_calls)]
     sage.quantize_qkv_rope(g.q, g.k, g.v, nr, rbuf, stream)
     for e in er:
         # each in-place transform starts from the workload's own Q and K (transforming the same buffer again

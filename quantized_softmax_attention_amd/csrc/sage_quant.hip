@@ -131,10 +131,6 @@ __device__ __forceinline__ void widen8(uint4 v, float (&x)[8]) {
     }
 }
 
-__device__ __forceinline__ void load_row8(const uint16_t *p, bool valid, float (&x)[8]) {
-    widen8(load_raw8(p, valid), x);
-}
-
 // The raw rows of tokens tb * 64 + row + 16 i (i = 0..3) of head h of a view,
 // thread (row, seg) = (t / 16, t % 16) holding channels 8 seg..+7.
 __device__ __forceinline__ void load_block_raw(View a, int b, int h, int tb, int N, uint4 (&raw)[4]) {
@@ -169,10 +165,12 @@ template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t a) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false);
 }
+// (mov_dpp: every lane is written by these patterns, so no old value is needed.)
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double a) {
     const uint64_t u = __double_as_longlong(a);
-    const uint32_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
     return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
@@ -267,22 +265,34 @@ __device__ __attribute__((noinline)) float ss_exact_lds(Row8 x, uint32_t *w, int
     return __uint_as_float(sq_words_to_f32(w));
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// The smallest nonzero bf16 magnitude field (15 bits, ordered like the values)
+// of 8 packed values, minus one; 0xFFFF when all are zero.  Packed 16-bit
+// integer operations, two values per instruction: a zero field minus one wraps
+// to 0xFFFF and never sets the minimum.
+__device__ __forceinline__ uint32_t min_nonzero_mag_minus1(uint4 raw) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    u16x2 m = u16x2{0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+        m = __builtin_elementwise_min(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu) - u16x2{1, 1});
+    return min((uint32_t)m.x, (uint32_t)m.y);
+}
+
 // ss of one row whose 8 values this lane holds (all 16 lanes of the row call it).
 __device__ __forceinline__ float row_sum_squares(uint4 raw, uint32_t *words, int seg) {
     float x[8];
     widen8(raw, x);
-    uint32_t lo = 0xFFFFFFFFu;
     double s = 0.0;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const uint32_t mag = (__float_as_uint(x[j]) >> 16) & 0x7FFFu;   // bf16 magnitude bits (ordered)
-        lo = min(lo, mag - 1u);                             // 0 -> 0xFFFFFFFF: zeros never set the minimum
         const double d = (double)x[j];
         s = __builtin_fma(d, d, s);                         // the squares are exact in fp64
     }
-    lo = row16_min_u32(lo);
+    const uint32_t lo = row16_min_u32(min_nonzero_mag_minus1(raw));
     s = row16_sum_f64(s);
-    if (lo == 0xFFFFFFFFu) return 0.0f;                     // an all-zero row
+    if (lo == 0xFFFFu) return 0.0f;                         // an all-zero row
     const int emin = max((int)((lo + 1u) >> 7), 1);          // subnormals count as exponent 1
     const int e = (int)(__double_as_longlong(s) >> 52) - 1023;   // s >= 2^-266 > 0: a normal fp64
     if (e + 1 - (2 * emin - 268) <= 53) return (float)s;   // exact fp64 sum, rounded once
@@ -434,10 +444,20 @@ __global__ __launch_bounds__(256) void norm_rope_kernel(OutView q, OutView k, in
 }
 
 // ------------------------------------------------------------- INT8 blocks
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+// The wave's largest value of a non-negative float (no NaN): the bit patterns of
+// such floats order like the values, so integer maxima decide it: DPP within each
+// 16-lane row, then the four rows' results read as scalars.
+__device__ __forceinline__ float wave_max_nonneg(float v) {
+    uint32_t a = __float_as_uint(v);
+    a = max(a, dpp_u32<0xB1>(a));    // quad_perm [1, 0, 3, 2]
+    a = max(a, dpp_u32<0x4E>(a));    // quad_perm [2, 3, 0, 1]
+    a = max(a, dpp_u32<0x141>(a));   // row_half_mirror
+    a = max(a, dpp_u32<0x140>(a));   // row_mirror
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)a, 0);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)a, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)a, 32);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)a, 48);
+    return __uint_as_float(max(max(r0, r1), max(r2, r3)));
 }
 
 // The codes are defined on the IEEE quotient x / scale.  Per element it is
@@ -468,12 +488,13 @@ __device__ __forceinline__ uint32_t int8_code(float x, float scale) {
     return (uint32_t)((int32_t)r) & 0xFFu;
 }
 
-// Workgroup-wide maxima of M per-thread values (256 threads, 4 waves) with one
-// barrier pair; red is M x 4 floats of LDS.  Every thread gets every maximum.
+// Workgroup-wide maxima of M non-negative per-thread values (256 threads, 4
+// waves) with one barrier pair; red is M x 4 floats of LDS.  Every thread gets
+// every maximum.
 template <int M>
 __device__ __forceinline__ void block_maxes(float (&m)[M], float (*red)[4]) {
 #pragma unroll
-    for (int i = 0; i < M; i++) m[i] = wave_max(m[i]);
+    for (int i = 0; i < M; i++) m[i] = wave_max_nonneg(m[i]);
     if ((threadIdx.x & 63) == 0)
 #pragma unroll
         for (int i = 0; i < M; i++) red[i][threadIdx.x >> 6] = m[i];
@@ -484,19 +505,23 @@ __device__ __forceinline__ void block_maxes(float (&m)[M], float (*red)[4]) {
 }
 
 // The INT8 blocks of one 64-token block tb of one head, thread t holding
-// channels 8*(t%16)..+7 of tokens t/16 + 16*i, i = 0..3 (x, already widened;
-// tokens >= N hold zeros, which changes no block maximum and yields zero
-// codes).  Q: two 32-token blocks (i < 2 and i >= 2); K: one 64-token block.
-__device__ __forceinline__ void q_local_max(const float (&x)[4][8], float &m0, float &m1) {
-    m0 = 0.0f;
-    m1 = 0.0f;
+// channels 8*(t%16)..+7 of tokens t/16 + 16*i, i = 0..3 (tokens >= N hold
+// zeros, which changes no block maximum and yields zero codes).  Q: two 32-token
+// blocks (i < 2 and i >= 2); K: one 64-token block.
+//
+// The largest |v| of packed bf16 rows I0 <= i < I1, as fp32: the 15-bit magnitude
+// fields compared as 16-bit integers, two per instruction (they order like the
+// magnitudes for every non-NaN value).
+template <int I0, int I1>
+__device__ __forceinline__ float absmax_bf16_rows(const uint4 (&rows)[4]) {
+    u16x2 m = u16x2{0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = I0; i < I1; i++) {
+        const uint32_t w[4] = {rows[i].x, rows[i].y, rows[i].z, rows[i].w};
 #pragma unroll
-        for (int j = 0; j < 8; j++) {
-            if (i < 2) m0 = fmaxf(m0, fabsf(x[i][j]));
-            else m1 = fmaxf(m1, fabsf(x[i][j]));
-        }
+        for (int j = 0; j < 4; j++) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu));
+    }
+    return __uint_as_float(max((uint32_t)m.x, (uint32_t)m.y) << 16);
 }
 __device__ __forceinline__ float k_local_max(const float (&x)[4][8]) {
     float m = 0.0f;
@@ -581,16 +606,6 @@ __device__ __forceinline__ void k_smoothed(const uint4 (&raw)[4], int tb, int N,
     }
 }
 
-__device__ __forceinline__ void load_block(View a, int b, int h, int tb, int N, float (&x)[4][8]) {
-    const int t = threadIdx.x, row = t >> 4, seg = t & 15;
-    const uint16_t *base = a.data + (int64_t)b * a.sb + (int64_t)h * a.sh + seg * 8;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int n = tb * 64 + row + 16 * i;
-        load_row8(base + (int64_t)n * a.sn, n < N, x[i]);
-    }
-}
-
 // One workgroup per (64-token block tb, head h, batch b): two Q blocks of 32
 // tokens and one K block of 64.
 __global__ __launch_bounds__(256) void quant_qk_kernel(View q, View k, int N, int H, int64_t Npad,
@@ -601,13 +616,13 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(View q, View k, int N, in
     const int tb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * H + h;
     float xq[4][8], xk[4][8];
-    uint4 rk[4];
+    uint4 rk[4], rq[4];
     load_block_raw(k, b, h, tb, N, rk);
-    load_block(q, b, h, tb, N, xq);
+    load_block_raw(q, b, h, tb, N, rq);
     k_smoothed<false>(rk, tb, N, km, bh, NormRope{}, nullptr, Npad, xk);
-    float m[3];
-    q_local_max(xq, m[0], m[1]);
-    m[2] = k_local_max(xk);
+#pragma unroll
+    for (int i = 0; i < 4; i++) widen8(rq[i], xq[i]);
+    float m[3] = {absmax_bf16_rows<0, 2>(rq), absmax_bf16_rows<2, 4>(rq), k_local_max(xk)};
     block_maxes(m, red);
     const float sq0 = m[0] / 127.0f, sq1 = m[1] / 127.0f, sk = m[2] / 127.0f;
     store_int8_codes(xq, sq0, sq1, tb, bh, Npad, qc);
@@ -761,12 +776,14 @@ __device__ __forceinline__ void v_block_max(const uint4 (&rv)[4], float (*vred)[
 }
 
 // The two Q blocks' scales (workgroup maxima / 127) and codes of the 64-token
-// block held in xq (rows row + 16 i).
-__device__ __forceinline__ void q_codes_and_scales(const float (&xq)[4][8], int tb, int64_t bh, int64_t Npad,
+// block held in rq (packed bf16, rows row + 16 i).
+__device__ __forceinline__ void q_codes_and_scales(const uint4 (&rq)[4], int tb, int64_t bh, int64_t Npad,
                                                    int8_t *__restrict__ qc, float *__restrict__ qs,
                                                    float (*red)[4]) {
-    float m[2];
-    q_local_max(xq, m[0], m[1]);
+    float m[2] = {absmax_bf16_rows<0, 2>(rq), absmax_bf16_rows<2, 4>(rq)};
+    float xq[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) widen8(rq[i], xq[i]);
     block_maxes(m, red);
     const float sq0 = m[0] / 127.0f, sq1 = m[1] / 127.0f;
     store_int8_codes(xq, sq0, sq1, tb, bh, Npad, qc);
@@ -815,13 +832,9 @@ __global__ __launch_bounds__(256) void qkv_pass1_kernel(View q, View k, View v, 
     load_block_raw(v, b, h, tb, N, rv);
     load_block_raw(q, b, h, tb, N, rq);
     v_block_max(rv, vred);
-    float xq[4][8];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        kbuf[row + 16 * i][seg] = rk[i];
-        widen8(rq[i], xq[i]);
-    }
-    q_codes_and_scales(xq, tb, bh, Npad, qc, qs, red);   // its barriers also publish kbuf and vred
+    for (int i = 0; i < 4; i++) kbuf[row + 16 * i][seg] = rk[i];
+    q_codes_and_scales(rq, tb, bh, Npad, qc, qs, red);   // its barriers also publish kbuf and vred
     if (tb >= nchunk) return;                        // a padding block: zero Q codes only
     k_sum_v_max_partials(kbuf, vred, b, tb, h, H, nchunk, wsk, wsv);
 }
@@ -852,10 +865,7 @@ __global__ __launch_bounds__(256) void qkv_rope_pass1_kernel(View q, View k, Vie
         uint4 rq[4];
         load_block_raw(q, b, h, tb, N, rq);
         norm_rope_rows<4>(rq, nr.gamma_q, nr.gamma_q, n, nr, N, y, r);
-        float xq[4][8];
-#pragma unroll
-        for (int i = 0; i < 4; i++) widen8(y[i], xq[i]);
-        q_codes_and_scales(xq, tb, bh, Npad, qc, qs, red);
+        q_codes_and_scales(y, tb, bh, Npad, qc, qs, red);
         return;
     }
     uint4 rk[4], rv[4];
