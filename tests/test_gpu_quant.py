@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from quantized_softmax_attention_amd import inputs, sage
 from tests import gpu_common as G
 
@@ -57,6 +58,34 @@ def test_quantizers_special_values():
     v[0, 3, 0, 12] = -(2.0 ** -30)
     case = inputs.Case("special", B, N, H, D, q.to(torch.bfloat16), x.to(torch.bfloat16), v.to(torch.bfloat16))
     _check_bitexact(case, G.OracleRef(case))
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["qk+v", "qkv"])
+def test_quantizers_unit_scale_ties(fused):
+    # Blocks whose scale is exactly 1 (amax 127 for INT8, 448 for E4M3), so every quotient is the value itself:
+    # exact ties k + 1/2 for the INT8 rounding, every E4M3 rounding boundary with both signs, both zeros, the
+    # boundary to zero 2^-10 and values next to it.  K pairs token n with N - 1 - n negated, so k_mean is
+    # exactly 0 and smoothing changes nothing.
+    B, N, H, D = 1, 300, 2, 128
+    g = torch.Generator().manual_seed(11)
+    ties = torch.arange(-127, 127, dtype=torch.float64) + 0.5            # 254 exact ties
+    q = ties[torch.randint(0, ties.numel(), (B, N, H, D), generator=g)]
+    q[0, ::32, :, 0] = 127.0                                              # every 32-token Q block: scale 1
+    half = ties[torch.randint(0, ties.numel(), (B, N // 2, H, D), generator=g)]
+    half[0, ::32, :, 1] = 127.0
+    k = torch.cat([half, -half.flip(1)], dim=1)                           # every 64-token K block: scale 1
+    table = torch.from_numpy(oracle.e4m3_decode(np.arange(0x7F)))
+    mids = (table[1:] + table[:-1]) / 2                                   # every rounding boundary
+    vals = torch.cat([table, mids, -table, -mids, torch.tensor([0.0, -0.0, 2.0 ** -10, -(2.0 ** -10),
+                                                                  3 * 2.0 ** -11, 2.0 ** -11])])
+    v = vals[torch.randint(0, vals.numel(), (B, N, H, D), generator=g)]
+    v[0, 5, :, :] = 448.0                                                 # every channel: scale 1
+    v[0, 6, 0, 3] = -0.0
+    case = inputs.Case("ties", B, N, H, D, q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16))
+    assert torch.equal(case.q.double(), q) and torch.equal(case.k.double(), k) and torch.equal(case.v.double(), v)
+    ref = G.OracleRef(case)
+    assert float(np.abs(ref.km).max()) == 0.0
+    _check_bitexact(case, ref, fused)
 
 
 def test_quantizers_repeatable():
