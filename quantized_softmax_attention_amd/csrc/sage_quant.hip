@@ -157,11 +157,6 @@ __device__ __forceinline__ void load_block_raw(View a, int b, int h, int tb, int
 
 // Lane-permuted copy of a within each 16-lane row (DPP; all lanes active).
 template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float a) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false));
-}
-
-template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t a) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false);
 }
