@@ -69,6 +69,24 @@ def test_attn_parity_ragged(N):
         assert np.allclose(got[:, :, 0], v0, rtol=2 ** -8, atol=0)
 
 
+def test_attn_parity_long_sequence():
+    # 4096 full 64-key tiles and a 37-key tail on two heads (seven times block-24's key walk, code buffers of
+    # 67 MB per head pair): the quantisers bit-exact over the whole tensor, the quantised and the bf16 paths on
+    # sampled rows against their oracles.
+    N = 4096 * 64 + 37
+    print("attention parity long sequence N =", N, flush=True)
+    case = inputs.packed_case(1, N, 2, seed=900)
+    ref = G.OracleRef(case)
+    gcase = G.gpu_case(case)
+    buf = G.run_quant(gcase)
+    G.check_quant_bitexact(buf, ref)
+    out, _ = G.run_attn(gcase, buf)
+    rows = _rows(case, (48, 16))
+    _gate(G.out_rows(out, rows), ref, rows, "N=%d" % N)
+    out16 = G.run_attn_bf16(gcase)
+    G.gate(G.out_rows(out16, rows), ref.exact(rows), 5e-3, "N=%d bf16 path vs exact" % N)
+
+
 @pytest.mark.parametrize("B,N,H", [(1, 4095, 1), (2, 300, 1)])
 def test_attn_parity_single_head(B, N, H):
     print("attention parity B=%d N=%d H=%d" % (B, N, H), flush=True)
