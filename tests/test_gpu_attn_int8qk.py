@@ -28,6 +28,19 @@ def _rows(case, spec):
     return inputs.sample_rows(case.B, case.H, case.N, count=spec[0], tail=spec[1])
 
 
+def test_int8qk_parity_long_sequence():
+    # 4096 full 64-key tiles and a 37-key tail on two heads
+    N = 4096 * 64 + 37
+    print("int8qk parity long sequence N =", N, flush=True)
+    case = inputs.packed_case(1, N, 2, seed=901)
+    ref = G.OracleRef(case)
+    out, _ = G.run_attn_int8qk(G.gpu_case(case))
+    rows = _rows(case, (48, 16))
+    got = G.out_rows(out, rows)
+    G.gate(got, G.bf16_round(ref.int8qk(rows)), 1e-3, "N=%d vs int8qk oracle" % N)
+    assert G.rel_l2(got, ref.exact(rows)) <= 2e-2
+
+
 @pytest.mark.parametrize("name", ["tiny", "mid", "block24", "stress"])
 def test_int8qk_parity_workloads(name):
     print("int8qk parity:", name, flush=True)

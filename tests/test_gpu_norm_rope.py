@@ -48,6 +48,7 @@ CASES = {
     "n65": lambda: inputs.packed_case(1, 65, 4, seed=33),
     "block24": lambda: inputs.config("block24"),
     "stress": lambda: inputs.config("stress"),        # B=2, x10 outlier channels, Student-t V
+    "long": lambda: inputs.packed_case(1, 4096 * 64 + 37, 2, seed=34),   # 4096 full blocks + a ragged tail
 }
 
 
