@@ -87,6 +87,24 @@ def test_attn_parity_long_sequence():
     G.gate(G.out_rows(out16, rows), ref.exact(rows), 5e-3, "N=%d bf16 path vs exact" % N)
 
 
+@pytest.mark.parametrize("B,N,H", [(1, 65, 4096), (96, 70, 3)])
+def test_many_heads_and_sequences(B, N, H):
+    # large head and batch indices in every kernel's addressing: the quantisers (separate and one-call) bit-exact,
+    # the quantised attention on every row against the method oracle, the bf16 path against exact
+    print("many heads / sequences: B=%d N=%d H=%d" % (B, N, H), flush=True)
+    case = inputs.packed_case(B, N, H, seed=950 + H)
+    ref = G.OracleRef(case)
+    gcase = G.gpu_case(case)
+    G.check_quant_bitexact(G.run_quant(gcase, True), ref)
+    buf = G.run_quant(gcase)
+    G.check_quant_bitexact(buf, ref)
+    out, _ = G.run_attn(gcase, buf)
+    rows = _rows(case, None)
+    G.gate(G.out_rows(out, rows), G.bf16_round(ref.method(rows)), 1e-3, "B=%d N=%d H=%d" % (B, N, H))
+    out16 = G.run_attn_bf16(gcase)
+    G.gate(G.out_rows(out16, rows), ref.exact(rows), 5e-3, "B=%d N=%d H=%d bf16 path vs exact" % (B, N, H))
+
+
 @pytest.mark.parametrize("B,N,H", [(1, 4095, 1), (2, 300, 1)])
 def test_attn_parity_single_head(B, N, H):
     print("attention parity B=%d N=%d H=%d" % (B, N, H), flush=True)
