@@ -49,6 +49,7 @@ CASES = {
     "block24": lambda: inputs.config("block24"),
     "stress": lambda: inputs.config("stress"),        # B=2, x10 outlier channels, Student-t V
     "long": lambda: inputs.packed_case(1, 4096 * 64 + 37, 2, seed=34),   # 4096 full blocks + a ragged tail
+    "many_heads": lambda: inputs.packed_case(3, 65, 700, seed=35),       # large (b, h) indices, ragged N
 }
 
 
