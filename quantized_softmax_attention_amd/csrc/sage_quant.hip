@@ -529,8 +529,9 @@ __device__ __forceinline__ float k_local_max(const float (&x)[4][8]) {
 
 // The INT8 code of x / scale for a block scale scale = RN(m / 127) >= kFastDivMin,
 // m the largest |x| of the block, in the low byte of the result.  Then
-// |x / scale| <= 127 (1 + 2^-24), so the correctly rounded quotient q rounds to an
-// integer in [-127, 127] (no clamp), and q + 1.5 * 2^23 lies in [2^23, 2^24),
+// |x / scale| < 127 (1 + 2^-23), so the correctly rounded quotient q is below
+// 127.5 in magnitude and rounds to an integer in [-127, 127] (no clamp), and
+// q + 1.5 * 2^23 lies in [2^23, 2^24),
 // where fp32 values are the integers: that one addition rounds q to nearest even,
 // and the sum is rint(q) + 1.5 * 2^23, whose low byte is rint(q) in two's
 // complement.  (The sign of a zero quotient does not matter: both give code 0.)
@@ -694,8 +695,8 @@ __device__ __forceinline__ void v_tile_codes(const uint4 (&raw)[4], int tt, int 
 #pragma unroll
     for (int j = 0; j < 8; j++) fast = fast && sv[j] >= kFastDivMin;
     if (fast) {
-        // sv = RN(amax / 448) is normal here, so every quotient has |y| <= 448 (1 + 2^-23):
-        // no saturation, and the conversion instruction rounds it as the E4M3 codec does
+        // sv = RN(amax / 448) is normal here, so every quotient has |y| < 448 (1 + 2^-22),
+        // below 464: no saturation, and the conversion instruction rounds it as the E4M3 codec does
         // (checked against the codec over that range, both zeros and fp32 subnormals,
         // by the instruction probe tests).  Keys 4g, 4g + 1 fill bytes 0, 1 and keys
         // 4g + 2, 4g + 3 bytes 2, 3.  Rows past N were loaded as +0: their codes are 0.
